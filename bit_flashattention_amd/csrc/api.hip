@@ -1,0 +1,266 @@
+// C ABI of the library (declared in include/hifa4.h): argument validation,
+// kernel selection and launch on the caller's stream.  The operation is the
+// HiFA4 attention operator (arXiv 2607.04302, Abstract); this file adds no
+// arithmetic of its own except the host-side finalization of the Smooth-QK
+// scales from the device-reduced maxima.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/hifa4.h"
+#include "hifa4_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+hifa4_status fail(hifa4_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hifa4_status ok() {
+  g_err[0] = '\0';
+  return HIFA4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+hifa4_status check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0) return fail(HIFA4_ENODEV, "no HIP device visible");
+  return HIFA4_OK;
+}
+
+// Device memory check for a caller buffer (NULL is accepted: callers check
+// presence separately).  Host and unregistered pointers are rejected.
+hifa4_status check_dev_ptr(const void* p, const char* name) {
+  if (!p) return HIFA4_OK;
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+    return fail(HIFA4_EINVAL, "%s is not a device pointer", name);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(HIFA4_EINVAL, "%s is not device memory", name);
+  return HIFA4_OK;
+}
+
+hifa4_status hip_fail(hipError_t e, const char* what) {
+  return fail(HIFA4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_d(int64_t d) { return d == 64 || d == 128 || d == 256; }
+
+}  // namespace
+
+extern "C" {
+
+int hifa4_version(void) { return 100; }
+
+const char* hifa4_status_str(hifa4_status s) {
+  switch (s) {
+    case HIFA4_OK: return "ok";
+    case HIFA4_EINVAL: return "invalid argument";
+    case HIFA4_EUNSUPPORTED: return "unsupported configuration";
+    case HIFA4_ENODEV: return "no HIP device";
+    case HIFA4_EHIP: return "HIP error";
+    case HIFA4_ENOSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* hifa4_last_error(void) { return g_err; }
+
+hifa4_status hifa4_mx4_bytes(int v_layout, int64_t B, int64_t H, int64_t N, int64_t d,
+                             size_t* code_bytes, size_t* scale_bytes) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || d % 32 != 0 || !code_bytes || !scale_bytes)
+    return fail(HIFA4_EINVAL, "mx4_bytes: need B, H, N >= 0, d > 0 a multiple of 32, outputs");
+  (void)v_layout;  // both layouts hold the same number of codes and scales
+  const int64_t np = hifa4::pad_tokens(N);
+  *code_bytes = (size_t)(B * H * np * (d / 2));
+  *scale_bytes = (size_t)(B * H * np * (d / 32));
+  return ok();
+}
+
+hifa4_status hifa4_calibrate_smooth(const void* q_cal_f16, const void* k_cal_f16, int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t N_cal, int64_t d,
+                                    float alpha, float* s_out, float* inv_s_out, void* stream) {
+  if (!q_cal_f16 || !k_cal_f16 || !s_out || !inv_s_out)
+    return fail(HIFA4_EINVAL, "calibrate: NULL buffer");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N_cal <= 0 || d <= 0 || Hq % Hkv != 0)
+    return fail(HIFA4_EINVAL, "calibrate: need positive sizes and Hq %% Hkv == 0");
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(HIFA4_EINVAL, "calibrate: alpha must be in [0, 1]");
+  if (!aligned(s_out, 4) || !aligned(inv_s_out, 4)) return fail(HIFA4_EINVAL, "calibrate: misaligned output");
+  hifa4_status st = check_device();
+  if (st) return st;
+  if ((st = check_dev_ptr(q_cal_f16, "q_cal")) || (st = check_dev_ptr(k_cal_f16, "k_cal")) ||
+      (st = check_dev_ptr(s_out, "s_out")) || (st = check_dev_ptr(inv_s_out, "inv_s_out")))
+    return st;
+  hipStream_t hs = (hipStream_t)stream;
+  // maxima land in the output buffers, are finalized on the host, then overwritten
+  hipError_t e = hifa4::launch_calib_absmax(q_cal_f16, k_cal_f16, B, Hq, Hkv, N_cal, d, s_out,
+                                            inv_s_out, hs);
+  if (e != hipSuccess) return hip_fail(e, "calibrate launch");
+  const size_t n = (size_t)(Hkv * d);
+  std::vector<float> qmax(n), kmax(n), s(n), inv(n);
+  if ((e = hipMemcpyAsync(qmax.data(), s_out, n * 4, hipMemcpyDeviceToHost, hs)) != hipSuccess ||
+      (e = hipMemcpyAsync(kmax.data(), inv_s_out, n * 4, hipMemcpyDeviceToHost, hs)) != hipSuccess ||
+      (e = hipStreamSynchronize(hs)) != hipSuccess)
+    return hip_fail(e, "calibrate copy-out");
+  for (size_t i = 0; i < n; i++) {
+    float sj = 1.0f;
+    if (qmax[i] > 0.0f && kmax[i] > 0.0f)
+      sj = (float)(std::pow((double)kmax[i], (double)alpha) / std::pow((double)qmax[i], 1.0 - (double)alpha));
+    s[i] = sj;
+    inv[i] = (float)(1.0 / (double)sj);
+  }
+  if ((e = hipMemcpyAsync(s_out, s.data(), n * 4, hipMemcpyHostToDevice, hs)) != hipSuccess ||
+      (e = hipMemcpyAsync(inv_s_out, inv.data(), n * 4, hipMemcpyHostToDevice, hs)) != hipSuccess ||
+      (e = hipStreamSynchronize(hs)) != hipSuccess)
+    return hip_fail(e, "calibrate copy-in");
+  return ok();
+}
+
+hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void* v_f16,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                                int64_t d, int smooth, const float* s, const float* inv_s,
+                                uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes,
+                                uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
+                                void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || N_q < 0 || N_kv < 0 || Hq % Hkv != 0)
+    return fail(HIFA4_EINVAL, "quantize: need B, N >= 0, Hq, Hkv > 0, Hq %% Hkv == 0");
+  if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "quantize: d must be a positive multiple of 32");
+  if (smooth && ((q_f16 && !s) || (k_f16 && !inv_s)))
+    return fail(HIFA4_EINVAL, "quantize: smooth = 1 needs s (for Q) and inv_s (for K)");
+  if ((q_f16 && (!q_codes || !q_scales)) || (k_f16 && (!k_codes || !k_scales)) ||
+      (v_f16 && (!v_codes || !v_scales)))
+    return fail(HIFA4_EINVAL, "quantize: missing output buffer");
+  const void* in[3] = {q_f16, k_f16, v_f16};
+  for (int i = 0; i < 3; i++)
+    if (in[i] && !aligned(in[i], 16)) return fail(HIFA4_EINVAL, "quantize: input not 16-byte aligned");
+  if ((q_f16 && (!aligned(q_codes, 16) || !aligned(q_scales, 4))) ||
+      (k_f16 && (!aligned(k_codes, 16) || !aligned(k_scales, 4))) ||
+      (v_f16 && (!aligned(v_codes, 16) || !aligned(v_scales, 4))) ||
+      (smooth && ((s && !aligned(s, 16)) || (inv_s && !aligned(inv_s, 16)))))
+    return fail(HIFA4_EINVAL, "quantize: misaligned buffer");
+  hifa4_status st = check_device();
+  if (st) return st;
+  const void* ptrs[] = {q_f16, k_f16, v_f16, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales,
+                        smooth ? s : nullptr, smooth ? inv_s : nullptr};
+  const char* names[] = {"q", "k", "v", "q_codes", "q_scales", "k_codes", "k_scales", "v_codes",
+                         "v_scales", "s", "inv_s"};
+  for (int i = 0; i < 11; i++)
+    if ((st = check_dev_ptr(ptrs[i], names[i]))) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  if (q_f16 && (e = hifa4::launch_quant_rows(q_f16, smooth ? s : nullptr, B, Hq, Hkv, N_q, d,
+                                              q_codes, q_scales, hs)) != hipSuccess)
+    return hip_fail(e, "quantize Q");
+  if (k_f16 && (e = hifa4::launch_quant_rows(k_f16, smooth ? inv_s : nullptr, B, Hkv, Hkv, N_kv, d,
+                                              k_codes, k_scales, hs)) != hipSuccess)
+    return hip_fail(e, "quantize K");
+  if (v_f16 && (e = hifa4::launch_quant_v(v_f16, B, Hkv, N_kv, d, v_codes, v_scales, hs)) != hipSuccess)
+    return hip_fail(e, "quantize V");
+  return ok();
+}
+
+hifa4_status hifa4_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t N_q, int64_t d,
+                                        int num_splits, size_t* bytes) {
+  if (!bytes || B < 0 || Hq < 0 || N_q < 0 || d <= 0 || num_splits < 1)
+    return fail(HIFA4_EINVAL, "workspace_bytes: bad arguments");
+  *bytes = num_splits > 1 ? (size_t)(B * Hq * N_q * num_splits * (d + 2)) * sizeof(float) : 0;
+  return ok();
+}
+
+hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                            int64_t d, int causal, int smooth, int reorder,
+                            const hifa4_attn_args* a, void* stream) {
+  if (!a) return fail(HIFA4_EINVAL, "attn: NULL args");
+  if (B < 0 || N_q < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(HIFA4_EINVAL, "attn: need B, N_q >= 0, Hq, Hkv > 0 and Hq %% Hkv == 0");
+  if (N_kv < 1 || N_kv > HIFA4_MAX_NKV)
+    return fail(HIFA4_EINVAL, "attn: N_kv must be in [1, %d]", HIFA4_MAX_NKV);
+  if (causal && N_q > N_kv) return fail(HIFA4_EINVAL, "attn: causal needs N_q <= N_kv");
+  if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "attn: d must be a positive multiple of 32");
+  if (!supported_d(d)) return fail(HIFA4_EUNSUPPORTED, "attn: d = %lld not built (64, 128, 256)", (long long)d);
+  if (B == 0 || N_q == 0) return ok();  // nothing to compute
+  const int kv_tile = a->kv_tile == 0 ? hifa4::kKvTile : a->kv_tile;
+  if (kv_tile != hifa4::kKvTile) return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64");
+  if (a->num_splits < 1) return fail(HIFA4_EINVAL, "attn: num_splits must be >= 1");
+  const bool q4 = a->q_codes || a->q_scales;
+  if (q4 == (a->q_f16 != nullptr)) return fail(HIFA4_EINVAL, "attn: set exactly one of q codes/scales or q_f16");
+  if (q4 && (!a->q_codes || !a->q_scales)) return fail(HIFA4_EINVAL, "attn: q codes and scales go together");
+  if (a->q_f16 && smooth && !a->s) return fail(HIFA4_EINVAL, "attn: q_f16 with smooth = 1 needs s");
+  if (!a->k_codes || !a->k_scales || !a->v_codes || !a->v_scales || !a->out_f16)
+    return fail(HIFA4_EINVAL, "attn: missing K/V/out buffer");
+  if ((a->phat_codes != nullptr) != (a->phat_scales != nullptr))
+    return fail(HIFA4_EINVAL, "attn: phat codes and scales go together");
+  const int64_t G = Hq / Hkv;
+  const bool split_path = a->num_splits > 1 || a->q_f16 != nullptr;
+  if (split_path && G * N_q > hifa4::kRowsPerWave)
+    return fail(HIFA4_EUNSUPPORTED, "attn: split-KV / raw-Q path needs N_q * Hq/Hkv <= 32");
+  if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 8) ||
+      (a->q_codes && (!aligned(a->q_codes, 16) || !aligned(a->q_scales, 8))) ||
+      (a->q_f16 && !aligned(a->q_f16, 16)) || (a->s && !aligned(a->s, 16)) || !aligned(a->out_f16, 8) ||
+      (a->phat_codes && !aligned(a->phat_codes, 16)) || (a->workspace && !aligned(a->workspace, 16)))
+    return fail(HIFA4_EINVAL, "attn: misaligned buffer");
+  size_t need = 0;
+  hifa4_attn_workspace_bytes(B, Hq, N_q, d, a->num_splits, &need);
+  hifa4_status st = check_device();
+  if (st) return st;
+  const void* ptrs[] = {a->q_codes, a->q_scales, a->q_f16, a->s, a->k_codes, a->k_scales,
+                        a->v_codes, a->v_scales, a->out_f16, a->workspace, a->phat_codes,
+                        a->phat_scales};
+  const char* names[] = {"q_codes", "q_scales", "q_f16", "s", "k_codes", "k_scales", "v_codes",
+                         "v_scales", "out", "workspace", "phat_codes", "phat_scales"};
+  for (int i = 0; i < 12; i++)
+    if ((st = check_dev_ptr(ptrs[i], names[i]))) return st;
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+    return fail(HIFA4_ENOSPACE, "attn: workspace needs %zu bytes", need);
+
+  hifa4::AttnLaunch L;
+  L.q_codes = a->q_codes;
+  L.q_scales = a->q_scales;
+  L.q_f16 = (const uint16_t*)a->q_f16;
+  L.s = a->s;
+  L.k_codes = a->k_codes;
+  L.k_scales = a->k_scales;
+  L.v_codes = a->v_codes;
+  L.v_scales = a->v_scales;
+  L.out = (uint16_t*)a->out_f16;
+  L.phat_codes = a->phat_codes;
+  L.phat_scales = a->phat_scales;
+  L.ws_o = (float*)a->workspace;
+  L.ws_ml = a->workspace ? (float*)a->workspace + B * Hq * N_q * a->num_splits * d : nullptr;
+  L.B = B;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.N_q = N_q;
+  L.N_kv = N_kv;
+  L.d = d;
+  L.Npad_q = hifa4::pad_tokens(N_q);
+  L.Npad_kv = hifa4::pad_tokens(N_kv);
+  L.causal = causal ? 1 : 0;
+  L.smooth = smooth ? 1 : 0;
+  L.reorder = reorder ? 1 : 0;
+  L.num_splits = a->num_splits;
+  hipError_t e;
+  if (split_path) {
+    e = hifa4::launch_attn_split(L, (hipStream_t)stream);
+  } else {
+    e = hifa4::launch_attn_prefill(L, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "attn launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal declarations shared by the host side of the library (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hifa4 {
+
+constexpr int64_t kTokenPad = 128;  // HIFA4_TOKEN_PAD
+constexpr int kKvTile = 64;         // keys per tile (two 32-key S^T MFMA column blocks)
+constexpr int kRowsPerWave = 32;    // query rows (MFMA columns) per wavefront
+constexpr int kWavesPerBlock = 4;
+
+inline int64_t pad_tokens(int64_t n) { return (n + kTokenPad - 1) / kTokenPad * kTokenPad; }
+
+hipError_t launch_calib_absmax(const void* q, const void* k, int64_t B, int64_t Hq, int64_t Hkv,
+                               int64_t N, int64_t d, float* qmax, float* kmax,
+                               hipStream_t stream);
+hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_t H, int64_t Hkv,
+                             int64_t N, int64_t d, uint8_t* codes, uint8_t* scales,
+                             hipStream_t stream);
+hipError_t launch_quant_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
+                          uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+// Everything one attention launch needs (device pointers + sizes).
+struct AttnLaunch {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const uint16_t* q_f16;
+  const float* s;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  uint16_t* out;
+  uint8_t* phat_codes;
+  uint8_t* phat_scales;
+  float* ws_o;   // [rows][C][d] fp32 split partial O
+  float* ws_ml;  // [rows][C][2] split partial (m, l)
+  int64_t B, Hq, Hkv, N_q, N_kv, d;
+  int64_t Npad_q, Npad_kv;
+  int causal, smooth, reorder, num_splits;
+};
+
+hipError_t launch_attn_prefill(const AttnLaunch& a, hipStream_t stream);
+hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t stream);
+
+}  // namespace hifa4

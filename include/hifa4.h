@@ -1,0 +1,178 @@
+/*
+ * hifa4.h -- C ABI of the MI355X (gfx950) 4-bit FlashAttention forward.
+ *
+ * The operation is the attention operator of HiFA4 (arXiv 2607.04302,
+ * "HiFA4: Training-Free 4-bit FlashAttention on Ascend HIF4 NPUs for LLM
+ * Inference", Abstract): both QK^T and PV run as 4-bit block-scaled GEMMs, the
+ * online-softmax state (running max m and normalizer l) is held in FP16,
+ * Smooth-QK rescales Q and K per channel after RoPE with static calibrated
+ * scales, and P-Reordering sums the normalizer from the same quantized P_hat
+ * that feeds the PV GEMM.  The abstract names the HIF4 4-bit format without
+ * defining it; this library uses MXFP4 instead: E2M1 elements (magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6, sign in bit 3) with one E8M0 power-of-two scale
+ * 2^(k-127) per 32 elements along the contraction dimension.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named *_f16, codes, scales, s, inv_s, out and workspace are
+ *   DEVICE pointers (hipMalloc'd or equivalent) on the current HIP device.
+ *   The caller owns every buffer; the library allocates, frees and retains
+ *   nothing, and keeps no global mutable state (calls are reentrant).
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   work is enqueued on it; only hifa4_calibrate_smooth synchronizes.
+ * - Tensors are row-major.  Raw tensors are binary16, BHSD:
+ *   Q [B][Hq][N_q][d], K and V [B][Hkv][N_kv][d].  Query head h reads KV head
+ *   h / (Hq / Hkv).
+ * - 4-bit layouts (element 2i in the low nibble of byte i; Npad = N rounded
+ *   up to a multiple of HIFA4_TOKEN_PAD; padding is written as zero codes
+ *   with scale byte 0):
+ *     row layout (Q, K):   codes [B][H][Npad][d/2],  scales [B][H][Npad][d/32]
+ *                          (blocks of 32 consecutive channels of one token)
+ *     token layout (V):    codes [B][H][d][Npad/2],  scales [B][H][d][Npad/32]
+ *                          (blocks of 32 consecutive tokens of one channel)
+ * - Errors: argument checks run first, on the host, and touch no device:
+ *   HIFA4_EINVAL (bad sizes, NULL where a buffer is required, misaligned
+ *   pointers), HIFA4_EUNSUPPORTED (valid but not built: d not 64/128/256,
+ *   kv_tile other than 64).  Then HIFA4_ENODEV if no HIP device is visible,
+ *   HIFA4_EINVAL for a pointer that is not device memory, HIFA4_ENOSPACE for a
+ *   too-small workspace, HIFA4_EHIP if a launch fails.  hifa4_last_error()
+ *   returns a thread-local message for the last failing call.  No C++
+ *   exception crosses this interface.
+ */
+#ifndef HIFA4_H
+#define HIFA4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HIFA4_TOKEN_PAD 128
+#define HIFA4_MAX_NKV 32768 /* l <= 1.5 * N_kv must stay below binary16's 65504 */
+
+typedef enum {
+  HIFA4_OK = 0,
+  HIFA4_EINVAL = 1,
+  HIFA4_EUNSUPPORTED = 2,
+  HIFA4_ENODEV = 3,
+  HIFA4_EHIP = 4,
+  HIFA4_ENOSPACE = 5
+} hifa4_status;
+
+/* Version of this interface (major * 100 + minor). */
+int hifa4_version(void);
+const char* hifa4_status_str(hifa4_status s);
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* hifa4_last_error(void);
+
+/*
+ * Bytes of one 4-bit tensor in the row layout (v_layout = 0, Q and K) or the
+ * token layout (v_layout = 1, V), for B x H x N tokens of d channels.
+ * EINVAL for negative sizes or d not a multiple of 32.  Host only.
+ */
+hifa4_status hifa4_mx4_bytes(int v_layout, int64_t B, int64_t H, int64_t N, int64_t d,
+                             size_t* code_bytes, size_t* scale_bytes);
+
+/*
+ * Smooth-QK calibration (HiFA4 Abstract: a calibration-static per-channel
+ * equivalent rescale of Q and K after RoPE, with no online reduction at
+ * inference).  The scale rule is SmoothQuant's migration with strength alpha:
+ *   s[g][j]     = max|K_g,j|^alpha / max|Q_j|^(1 - alpha)
+ *   inv_s[g][j] = fp32(1 / s[g][j])
+ * with the maxima over all B x N_cal calibration tokens (for Q also over the
+ * Hq/Hkv query heads that share KV head g) and s = 1 where either maximum is
+ * 0.  The maxima are reduced on the device; s is finalized on the host in
+ * double and rounded once to fp32, so the call synchronizes `stream`.
+ * q_cal_f16 [B][Hq][N_cal][d], k_cal_f16 [B][Hkv][N_cal][d] binary16;
+ * s_out, inv_s_out [Hkv][d] fp32 (device).  alpha in [0, 1].
+ */
+hifa4_status hifa4_calibrate_smooth(const void* q_cal_f16, const void* k_cal_f16, int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t N_cal, int64_t d,
+                                    float alpha, float* s_out, float* inv_s_out, void* stream);
+
+/*
+ * Smooth-QK apply + 4-bit quantization (HiFA4 Abstract: Q*s and K/s after
+ * RoPE, then 4-bit operands for both GEMMs).
+ *   Q: x = fp32(q * s[g][j])      (smooth = 1) or fp32(q) (smooth = 0)
+ *   K: x = fp32(k * inv_s[g][j])  (a multiply by the stored reciprocal)
+ *   Each block of 32: e = clamp(floor(log2 max|x|) - 2, -127, 127) (all-zero
+ *   block: -127), scale byte e + 127, codes RNE_E2M1(x * 2^-e) with ties to
+ *   the even code and saturation at +-6.
+ *   V: no rescale; blocks of 32 consecutive tokens (token layout).
+ * Any of q_f16 / k_f16 / v_f16 may be NULL to skip that tensor (its output
+ * pointers are then ignored).  s and inv_s are [Hkv][d] fp32, ignored when
+ * smooth = 0.  Codes/scales buffers must hold hifa4_mx4_bytes(...) bytes and
+ * be 16-byte aligned (codes) / 4-byte aligned (scales).  Asynchronous.
+ */
+hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void* v_f16,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                                int64_t d, int smooth, const float* s, const float* inv_s,
+                                uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes,
+                                uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
+                                void* stream);
+
+/* Buffers of one attention call (all device pointers). */
+typedef struct {
+  /* Q: either 4-bit (row layout, from hifa4_quantize_qkv) ... */
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  /* ... or raw binary16 [B][Hq][N_q][d], smoothed with `s` (when smooth = 1)
+   * and quantized inside the kernel exactly as hifa4_quantize_qkv would. */
+  const void* q_f16;
+  const float* s;
+  /* K row layout, V token layout (from hifa4_quantize_qkv). */
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  /* Output [B][Hq][N_q][d] binary16. */
+  void* out_f16;
+  /* Scratch for split-KV partial states; hifa4_attn_workspace_bytes(). */
+  void* workspace;
+  size_t workspace_bytes;
+  /* Keys per tile (the tile partition fixes the FP16 state's rounding
+   * sequence).  0 selects the default, 64. */
+  int kv_tile;
+  /* Split-KV: 1 = one pass; C > 1 deals the ceil(N_kv/kv_tile) tiles to C
+   * chunks of consecutive tiles, each run from (-inf, 0, 0) and merged in
+   * chunk order with FP16 (m, l).  C > 1 requires N_q * Hq/Hkv <= 32. */
+  int num_splits;
+  /* Optional P_hat dump (NULL = off): codes [B][Hq][N_q][Npad_kv/2] and
+   * scales [B][Hq][N_q][Npad_kv/32] of every tile a row visits; entries of
+   * tiles a row never visits are left as the caller initialized them. */
+  uint8_t* phat_codes;
+  uint8_t* phat_scales;
+} hifa4_attn_args;
+
+/* Workspace bytes hifa4_attn_fwd needs for these sizes (0 when num_splits = 1). */
+hifa4_status hifa4_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t N_q, int64_t d,
+                                        int num_splits, size_t* bytes);
+
+/*
+ * 4-bit FlashAttention forward (HiFA4 Abstract).  Per query row, over tiles
+ * of kv_tile keys in ascending order (keys valid when j < N_kv and, if
+ * causal, j <= i + N_kv - N_q):
+ *   S      = Q_hat K_hat^T                          (4-bit GEMM, fp32 accumulation)
+ *   m_new  = fp16(max(m, fp32(c * max S))),  c = fp32(log2(e) / sqrt(d))
+ *   alpha  = 2^(m - m_new);   P = 2^(fma(S, c, -m_new))
+ *   P_hat  = per 32 keys: e = clamp(floor(max t) - 2, -127, 127), E2M1_rne(P / 2^e) * 2^e
+ *   reorder = 1 (P-Reordering): [O | l] = alpha * [O | l] + P_hat [V_hat | 1]
+ *                                (the normalizer is a column of the PV GEMM)
+ *   reorder = 0:                 O = alpha * O + P_hat V_hat,  l = alpha * l + sum P
+ *   l      = fp16(l)
+ *   out    = fp16(O / l)
+ * `smooth` states whether Q_hat/K_hat carry the Smooth-QK scales; with q_f16
+ * it makes the kernel multiply Q by s before quantizing.  d in {64, 128,
+ * 256}; N_kv in [1, HIFA4_MAX_NKV]; causal requires N_q <= N_kv; N_q = 0 or
+ * B = 0 is a successful no-op.  Asynchronous.
+ */
+hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                            int64_t d, int causal, int smooth, int reorder,
+                            const hifa4_attn_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HIFA4_H */

@@ -1,0 +1,57 @@
+"""Shared helpers for the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+# Acceptance bounds: >= 99.9 % identical 4-bit codes; output error relative to each
+# row's max |O_oracle| at most 1e-2 (max) and 1e-3 (mean).
+CODE_MATCH = 0.999
+ERR_MAX = 1e-2
+ERR_MEAN = 1e-3
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    if a.dtype == np.float16:
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_host(t) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def codes_equal(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per-nibble equality of packed E2M1 codes, with +0 (code 0) == -0 (code 8)."""
+    na, nb = oracle.unpack_nibbles(a), oracle.unpack_nibbles(b)
+    za = (na & 7) == 0
+    zb = (nb & 7) == 0
+    return (na == nb) | (za & zb)
+
+
+def code_match_fraction(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.mean(codes_equal(a, b)))
+
+
+def out_error(got_f16: np.ndarray, ref_f16: np.ndarray):
+    """(max, mean) of |got - ref| / max_row |ref| over rows of the last axis."""
+    g = got_f16.astype(np.float32).reshape(-1, got_f16.shape[-1]).astype(np.float64)
+    r = ref_f16.astype(np.float32).reshape(-1, ref_f16.shape[-1]).astype(np.float64)
+    rowmax = np.abs(r).max(axis=1, keepdims=True)
+    rowmax[rowmax == 0] = 1.0
+    e = np.abs(g - r) / rowmax
+    return float(e.max()), float(e.mean())
+
+
+def oracle_quant(w, s=None, inv=None):
+    q4 = oracle.quantize_rows(w.q, w.Hkv, s)
+    k4 = oracle.quantize_rows(w.k, w.Hkv, inv)
+    v4 = oracle.quantize_v(w.v)
+    return q4, k4, v4
+
+
+def mx4_to_dev(pair):
+    import bit_flashattention_amd as hf
+    return hf.MX4(to_dev(pair[0]), to_dev(pair[1]))

@@ -1,0 +1,163 @@
+"""The C-ABI library builds, loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hifa4.h")
+
+
+@pytest.fixture(scope="module")
+def hf():
+    import bit_flashattention_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from bit_flashattention_amd import build
+        build.build(verbose=False)
+    m.load()
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b(hifa4_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported(hf):
+    names = _declared()
+    assert set(hf.EXPORTS) == set(names)
+    lib = ctypes.CDLL(hf.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(hf):
+    lib = hf.load()
+    assert lib.hifa4_version() == 100
+    for s in range(6):
+        assert lib.hifa4_status_str(s)
+    assert b"unknown" in lib.hifa4_status_str(99)
+
+
+def test_mx4_bytes(hf):
+    assert hf.hifa4_mx4_bytes(0, 1, 32, 4096, 128) == (32 * 4096 * 64, 32 * 4096 * 4)
+    assert hf.hifa4_mx4_bytes(1, 2, 8, 100, 256) == (2 * 8 * 128 * 128, 2 * 8 * 128 * 8)
+    assert hf.hifa4_mx4_bytes(0, 0, 8, 0, 64) == (0, 0)
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_mx4_bytes(0, 1, 1, 1, 100)
+    assert e.value.status == hf.EINVAL
+
+
+def test_workspace_bytes(hf):
+    assert hf.hifa4_attn_workspace_bytes(64, 32, 1, 128, 1) == 0
+    assert hf.hifa4_attn_workspace_bytes(64, 32, 1, 128, 16) == 64 * 32 * 16 * 130 * 4
+    with pytest.raises(hf.HiFA4Error):
+        hf.hifa4_attn_workspace_bytes(1, 1, 1, 128, 0)
+
+
+def _args(hf, **kw):
+    a = hf.AttnArgs()
+    fake = 0x1000  # never dereferenced: every case below fails validation first
+    a.q_codes = a.q_scales = a.k_codes = a.k_scales = a.v_codes = a.v_scales = fake
+    a.out_f16 = fake
+    a.num_splits = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(Hq=6, Hkv=4), "EINVAL"),
+    (dict(N_kv=0), "EINVAL"),
+    (dict(N_kv=40000), "EINVAL"),
+    (dict(N_q=300, N_kv=256, causal=1), "EINVAL"),
+    (dict(d=100), "EINVAL"),
+    (dict(d=96), "EUNSUPPORTED"),
+    (dict(args=dict(kv_tile=128)), "EUNSUPPORTED"),
+    (dict(args=dict(num_splits=0)), "EINVAL"),
+    (dict(args=dict(q_f16=0x2000)), "EINVAL"),          # both Q forms given
+    (dict(args=dict(k_codes=None)), "EINVAL"),
+    (dict(args=dict(out_f16=None)), "EINVAL"),
+    (dict(args=dict(phat_codes=0x1000)), "EINVAL"),      # codes without scales
+    (dict(args=dict(num_splits=4), N_q=16), "EUNSUPPORTED"),  # 16 rows x 4 heads > 32
+    (dict(args=dict(k_codes=0x1008)), "EINVAL"),         # misaligned
+])
+def test_attn_validation(hf, case, status):
+    shape = dict(B=1, Hq=8, Hkv=2, N_q=64, N_kv=256, d=128, causal=0)
+    argkw = case.pop("args", {})
+    shape.update(case)
+    a = _args(hf, **argkw)
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_attn_fwd(shape["B"], shape["Hq"], shape["Hkv"], shape["N_q"], shape["N_kv"],
+                          shape["d"], shape["causal"], 0, 1, a, None)
+    assert e.value.status == getattr(hf, status)
+    assert hf.load().hifa4_last_error()
+
+
+def test_attn_empty_is_noop(hf):
+    a = _args(hf)
+    hf.hifa4_attn_fwd(1, 8, 2, 0, 256, 128, 0, 0, 1, a, None)
+    hf.hifa4_attn_fwd(0, 8, 2, 64, 256, 128, 0, 0, 1, a, None)
+
+
+def test_device_checks_after_validation(hf):
+    """Valid sizes with host pointers: ENODEV without a GPU, EINVAL (not device memory) with one."""
+    host = np.zeros(1 << 16, dtype=np.uint8)
+    p = host.ctypes.data
+    p = (p + 255) // 256 * 256
+    a = _args(hf, q_codes=p, q_scales=p, k_codes=p, k_scales=p, v_codes=p, v_scales=p, out_f16=p)
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_attn_fwd(1, 8, 2, 64, 256, 128, 1, 0, 1, a, None)
+    assert e.value.status in (hf.ENODEV, hf.EINVAL)
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 128, 0, None, None, p, p, None, None,
+                              None, None, None)
+    assert e.value.status in (hf.ENODEV, hf.EINVAL)
+
+
+@pytest.mark.parametrize("call", ["quant_smooth_no_s", "quant_bad_d", "quant_missing_out",
+                                  "calib_alpha", "calib_null"])
+def test_quantize_calibrate_validation(hf, call):
+    p = 0x10000
+    with pytest.raises(hf.HiFA4Error) as e:
+        if call == "quant_smooth_no_s":
+            hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 128, 1, None, None, p, p, None,
+                                  None, None, None, None)
+        elif call == "quant_bad_d":
+            hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 100, 0, None, None, p, p, None,
+                                  None, None, None, None)
+        elif call == "quant_missing_out":
+            hf.hifa4_quantize_qkv(None, p, None, 1, 8, 2, 0, 64, 128, 0, None, None, None, None,
+                                  None, None, None, None, None)
+        elif call == "calib_alpha":
+            hf.hifa4_calibrate_smooth(p, p, 1, 8, 2, 16, 128, 1.5, p, p, None)
+        else:
+            hf.hifa4_calibrate_smooth(p, None, 1, 8, 2, 16, 128, 0.5, p, p, None)
+    assert e.value.status == hf.EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    import bit_flashattention_amd as m
+    saved = m._lib
+    try:
+        m._lib = None
+        with pytest.raises(OSError):
+            m.load(str(tmp_path / "missing.so"))
+    finally:
+        m._lib = saved
+
+
+def test_product_path_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "bit_flashattention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "hifa4_oracle" not in txt, f

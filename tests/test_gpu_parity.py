@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: 100 % identical Q/K/V codes and scales (deterministic quantizer; +0 and
+-0 compare equal), >= 99.9 % identical P_hat codes, output error <= 1e-2 max
+and <= 1e-3 mean relative to each row's max |O_oracle|.  Inputs are the seeded
+synthetic workloads (scaled-down shapes with the benchmark's structure, plus
+ragged and degenerate cases).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import (CODE_MATCH, ERR_MAX, ERR_MEAN, code_match_fraction, codes_equal,
+                        mx4_to_dev, oracle_quant, out_error, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hf():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible HIP device")
+    import bit_flashattention_amd as m
+    m.load()
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# calibration + quantization
+# ---------------------------------------------------------------------------
+
+QUANT_CASES = [
+    ("single_head", dict()),
+    ("qwen3_8b", dict(B=1, Hq=8, Hkv=2, N=300, d=128, n_cal=200)),
+    ("gemma2_9b", dict(B=1, Hq=4, Hkv=2, N=130, d=256, n_cal=96)),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128)),
+    ("qwen3_8b", dict(B=2, Hq=2, Hkv=1, N=33, d=64, n_cal=40)),
+]
+
+
+@pytest.mark.parametrize("name,kw", QUANT_CASES)
+def test_calibrate_and_quantize_match_oracle(hf, name, kw):
+    print(f"[quantize] {name} {kw}", flush=True)
+    w = synth.WORKLOADS[name](**kw)
+    if w.smooth:
+        s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+        s, inv = hf.calibrate_smooth(to_dev(w.q_cal), to_dev(w.k_cal), w.alpha)
+        assert np.array_equal(to_host(s), s_ref)
+        assert np.array_equal(to_host(inv), inv_ref)
+    else:
+        s_ref = inv_ref = s = inv = None
+    q4, k4, v4 = hf.quantize_qkv(to_dev(w.q), to_dev(w.k), to_dev(w.v), Hkv=w.Hkv,
+                                 smooth=w.smooth, s=s, inv_s=inv)
+    _sync()
+    rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
+    for got, ref in ((q4, rq), (k4, rk), (v4, rv)):
+        assert np.all(codes_equal(to_host(got.codes), ref[0]))
+        assert np.array_equal(to_host(got.scales), ref[1])
+
+
+def test_quantize_edge_values(hf):
+    """Zero blocks, subnormal binary16, saturating and tiny blocks."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((1, 2, 64, 128)) * 3).astype(np.float16)
+    x[0, 0, 0, :32] = 0                                   # all-zero block -> scale byte 0
+    x[0, 0, 1, :32] = np.float16(2.0 ** -24)              # subnormal binary16 block
+    x[0, 0, 2, :32] = np.float16(-0.0)
+    x[0, 0, 3, 32:64] = np.float16(60000.0)               # large
+    x[0, 1, 5, :] = np.float16(7.9)                        # clip [6, 8) * 2^e -> 6
+    x[0, 1, 6, 64:96] = np.linspace(-1, 1, 32).astype(np.float16)
+    s = np.ones((1, 128), dtype=np.float32)
+    s[0, :32] = 2.0 ** -120                                # drives products subnormal in fp32
+    inv = (1.0 / s).astype(np.float32)
+    q4, k4, _ = hf.quantize_qkv(to_dev(x), to_dev(x[:, :1]), None, Hkv=1, smooth=True,
+                                s=to_dev(s), inv_s=to_dev(inv))
+    _sync()
+    rq = oracle.quantize_rows(x, 1, s)
+    rk = oracle.quantize_rows(x[:, :1], 1, inv)
+    assert np.all(codes_equal(to_host(q4.codes), rq[0]))
+    assert np.array_equal(to_host(q4.scales), rq[1])
+    assert np.all(codes_equal(to_host(k4.codes), rk[0]))
+    assert np.array_equal(to_host(k4.scales), rk[1])
+    v = x.copy()
+    _, _, v4 = hf.quantize_qkv(None, None, to_dev(v), Hkv=2)
+    _sync()
+    rv = oracle.quantize_v(v)
+    assert np.all(codes_equal(to_host(v4.codes), rv[0]))
+    assert np.array_equal(to_host(v4.scales), rv[1])
+
+
+# ---------------------------------------------------------------------------
+# attention forward
+# ---------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # name, overrides, reorder
+    ("single_head", dict(), 1),
+    ("single_head", dict(), 0),
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 1),
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 0),
+    ("qwen3_8b", dict(B=1, Hq=2, Hkv=2, N=200, N_kv=330, d=128, n_cal=64), 1),  # ragged, N_q < N_kv
+    ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=384, d=256, n_cal=128), 1),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 1),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 0),
+    ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1),
+]
+
+
+def _prefill_case(hf, w, reorder, dump=True):
+    import torch
+    if w.smooth:
+        s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    else:
+        s_ref = inv_ref = None
+    rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
+    q4, k4, v4 = mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv)
+    phat = None
+    npk = oracle.padded(w.N_kv)
+    if dump:
+        phat = hf.MX4(torch.zeros((w.B, w.Hq, w.N_q, npk // 2), dtype=torch.uint8, device="cuda"),
+                      torch.zeros((w.B, w.Hq, w.N_q, npk // 32), dtype=torch.uint8, device="cuda"))
+    out = hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
+                      causal=w.causal, smooth=w.smooth, reorder=reorder, phat=phat)
+    _sync()
+    ref = oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=reorder,
+                      kv_tile=64, q4=rq, k4=rk, v4=rv, want_phat=dump)
+    return out, phat, ref
+
+
+@pytest.mark.parametrize("name,kw,reorder", ATTN_CASES)
+def test_prefill_matches_oracle(hf, name, kw, reorder):
+    print(f"[prefill] {name} {kw} reorder={reorder}", flush=True)
+    w = synth.WORKLOADS[name](**kw)
+    if name == "single_head":
+        w.causal = False
+    out, phat, ref = _prefill_case(hf, w, reorder)
+    got = to_host(out).reshape(-1, w.d).view(np.uint16)
+    frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
+    sc = np.mean(to_host(phat.scales).reshape(len(got), -1) == ref["phat_scales"])
+    emax, emean = out_error(got.view(np.float16), ref["out"].view(np.float16))
+    print(f"  P_hat code match {frac:.6f}, scale match {sc:.6f}, err max {emax:.2e} mean {emean:.2e}")
+    assert frac >= CODE_MATCH
+    assert sc >= CODE_MATCH
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
+
+
+def test_prefill_deterministic(hf):
+    w = synth.qwen3_8b(B=1, Hq=4, Hkv=1, N=256, d=128, n_cal=64)
+    a, _, _ = _prefill_case(hf, w, 1, dump=False)
+    b, _, _ = _prefill_case(hf, w, 1, dump=False)
+    assert np.array_equal(to_host(a).view(np.uint16), to_host(b).view(np.uint16))
+
+
+def test_v_ones_gives_one(hf):
+    """P-Reordering on the GPU: V = 1 yields output 1 up to the FP16 normalizer."""
+    import torch
+    w = synth.qwen3_8b(B=1, Hq=2, Hkv=1, N=256, d=128, n_cal=64)
+    w.v = np.ones_like(w.v)
+    out, _, _ = _prefill_case(hf, w, 1, dump=False)
+    o = to_host(out).astype(np.float32)
+    assert np.abs(o - 1).max() <= 4 * 2.0 ** -11 + 2.0 ** -11
+
+
+DECODE_CASES = [
+    dict(B=2, Hq=8, Hkv=2, N_kv=1000, d=128, num_splits=4),
+    dict(B=3, Hq=32, Hkv=8, N_kv=512, d=128, num_splits=1),
+    dict(B=2, Hq=4, Hkv=4, N_kv=700, d=64, num_splits=3),
+    dict(B=1, Hq=8, Hkv=1, N_kv=4096, d=256, num_splits=16),
+]
+
+
+@pytest.mark.parametrize("kw", DECODE_CASES)
+def test_decode_split_matches_oracle(hf, kw):
+    import torch
+    print(f"[decode] {kw}", flush=True)
+    kw = dict(kw)
+    C = kw.pop("num_splits")
+    w = synth.decode(n_cal=128, **kw)
+    s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
+    rv = oracle.quantize_v(w.v)
+    rq = oracle.quantize_rows(w.q, w.Hkv, s_ref)
+    npk = oracle.padded(w.N_kv)
+    phat = hf.MX4(torch.zeros((w.B, w.Hq, 1, npk // 2), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((w.B, w.Hq, 1, npk // 32), dtype=torch.uint8, device="cuda"))
+    out = hf.attn_fwd(None, mx4_to_dev(rk), mx4_to_dev(rv), B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=1,
+                      N_kv=w.N_kv, d=w.d, causal=False, smooth=True, reorder=True,
+                      q_f16=to_dev(w.q), s=to_dev(s_ref), num_splits=C, phat=phat)
+    _sync()
+    ref = oracle.attn(w.B, w.Hq, w.Hkv, 1, w.N_kv, w.d, causal=False, reorder=1, num_splits=C,
+                      q4=rq, k4=rk, v4=rv, want_phat=True)
+    got = to_host(out).reshape(-1, w.d)
+    frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
+    emax, emean = out_error(got, ref["out"].view(np.float16))
+    print(f"  P_hat code match {frac:.6f}, err max {emax:.2e} mean {emean:.2e}")
+    assert frac >= CODE_MATCH
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
+
+
+def test_split_path_with_prequantized_q_and_causal(hf):
+    """Split-KV with pre-quantized Q, several query rows (G * N_q <= 32) and a causal mask."""
+    w = synth.qwen3_8b(B=2, Hq=8, Hkv=2, N=4, N_kv=700, d=128, n_cal=64)
+    s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
+    out = hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv), B=2, Hq=8, Hkv=2, N_q=4,
+                      N_kv=700, d=128, causal=True, smooth=True, reorder=False, num_splits=5)
+    _sync()
+    ref = oracle.attn(2, 8, 2, 4, 700, 128, causal=True, reorder=0, num_splits=5, q4=rq, k4=rk,
+                      v4=rv)
+    emax, emean = out_error(to_host(out).reshape(-1, 128), ref["out"].view(np.float16))
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
+
+
+def test_empty_and_single_key(hf):
+    import torch
+    w = synth.qwen3_8b(B=1, Hq=2, Hkv=1, N=3, N_kv=1, d=128, n_cal=32)
+    rq, rk, rv = oracle_quant(w)
+    out = hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=3,
+                      N_kv=1, d=128, causal=False, smooth=False, reorder=True)
+    _sync()
+    ref = oracle.attn(1, 2, 1, 3, 1, 128, causal=False, reorder=1, q4=rq, k4=rk, v4=rv)
+    assert np.array_equal(to_host(out).reshape(-1, 128).view(np.uint16), ref["out"])
+    # N_q = 0: a successful no-op
+    empty = torch.empty((1, 2, 0, 128), dtype=torch.float16, device="cuda")
+    hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=0,
+                N_kv=1, d=128, causal=False, smooth=False, reorder=True, out=empty)
+    _sync()
