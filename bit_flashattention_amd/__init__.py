@@ -151,9 +151,9 @@ class MX4:
 def empty_mx4(v_layout: bool, B: int, H: int, N: int, d: int, device="cuda") -> MX4:
     import torch
     npad = padded(N)
-    if v_layout:
-        return MX4(torch.empty((B, H, d, npad // 2), dtype=torch.uint8, device=device),
-                   torch.empty((B, H, d, npad // 32), dtype=torch.uint8, device=device))
+    if v_layout:  # tiled token layout: [B][H][Npad/64][d][32] codes, [..][d][2] scales
+        return MX4(torch.empty((B, H, npad // 64, d, 32), dtype=torch.uint8, device=device),
+                   torch.empty((B, H, npad // 64, d, 2), dtype=torch.uint8, device=device))
     return MX4(torch.empty((B, H, npad, d // 2), dtype=torch.uint8, device=device),
                torch.empty((B, H, npad, d // 32), dtype=torch.uint8, device=device))
 
@@ -215,8 +215,8 @@ def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, w
 
 def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, N_q: int,
              N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool, q_f16=None, s=None,
-             num_splits: int = 1, out=None, workspace=None, phat: Optional[MX4] = None,
-             stream=None):
+             num_splits: int = 1, kv_tile: int = 64, out=None, workspace=None,
+             phat: Optional[MX4] = None, stream=None):
     """4-bit attention forward; returns out [B][Hq][N_q][d] binary16."""
     import torch
     dev = k4.codes.device
@@ -226,6 +226,6 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
         nbytes = hifa4_attn_workspace_bytes(B, Hq, N_q, d, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=workspace,
-                     num_splits=num_splits, phat=phat)
+                     num_splits=num_splits, kv_tile=kv_tile, phat=phat)
     hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args, _stream(stream))
     return out

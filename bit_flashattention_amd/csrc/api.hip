@@ -147,9 +147,9 @@ hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void
   const void* in[3] = {q_f16, k_f16, v_f16};
   for (int i = 0; i < 3; i++)
     if (in[i] && !aligned(in[i], 16)) return fail(HIFA4_EINVAL, "quantize: input not 16-byte aligned");
-  if ((q_f16 && (!aligned(q_codes, 16) || !aligned(q_scales, 4))) ||
-      (k_f16 && (!aligned(k_codes, 16) || !aligned(k_scales, 4))) ||
-      (v_f16 && (!aligned(v_codes, 16) || !aligned(v_scales, 4))) ||
+  if ((q_f16 && (!aligned(q_codes, 16) || !aligned(q_scales, 16))) ||
+      (k_f16 && (!aligned(k_codes, 16) || !aligned(k_scales, 16))) ||
+      (v_f16 && (!aligned(v_codes, 16) || !aligned(v_scales, 16))) ||
       (smooth && ((s && !aligned(s, 16)) || (inv_s && !aligned(inv_s, 16)))))
     return fail(HIFA4_EINVAL, "quantize: misaligned buffer");
   hifa4_status st = check_device();
@@ -194,7 +194,8 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   if (!supported_d(d)) return fail(HIFA4_EUNSUPPORTED, "attn: d = %lld not built (64, 128, 256)", (long long)d);
   if (B == 0 || N_q == 0) return ok();  // nothing to compute
   const int kv_tile = a->kv_tile == 0 ? hifa4::kKvTile : a->kv_tile;
-  if (kv_tile != hifa4::kKvTile) return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64");
+  if (kv_tile != 64 && !(kv_tile == 128 && d <= 128))
+    return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64 (or 128 with d <= 128)");
   if (a->num_splits < 1) return fail(HIFA4_EINVAL, "attn: num_splits must be >= 1");
   const bool q4 = a->q_codes || a->q_scales;
   if (q4 == (a->q_f16 != nullptr)) return fail(HIFA4_EINVAL, "attn: set exactly one of q codes/scales or q_f16");
@@ -208,7 +209,8 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   const bool split_path = a->num_splits > 1 || a->q_f16 != nullptr;
   if (split_path && G * N_q > hifa4::kRowsPerWave)
     return fail(HIFA4_EUNSUPPORTED, "attn: split-KV / raw-Q path needs N_q * Hq/Hkv <= 32");
-  if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 8) ||
+  if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 16) ||
+      !aligned(a->v_scales, 16) ||
       (a->q_codes && (!aligned(a->q_codes, 16) || !aligned(a->q_scales, 8))) ||
       (a->q_f16 && !aligned(a->q_f16, 16)) || (a->s && !aligned(a->s, 16)) || !aligned(a->out_f16, 8) ||
       (a->phat_codes && !aligned(a->phat_codes, 16)) || (a->workspace && !aligned(a->workspace, 16)))
@@ -253,6 +255,7 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   L.smooth = smooth ? 1 : 0;
   L.reorder = reorder ? 1 : 0;
   L.num_splits = a->num_splits;
+  L.kv_tile = kv_tile;
   hipError_t e;
   if (split_path) {
     e = hifa4::launch_attn_split(L, (hipStream_t)stream);

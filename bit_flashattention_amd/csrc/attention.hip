@@ -5,22 +5,31 @@
 // P-Reordering the normalizer is summed from the same quantized P_hat that
 // feeds the PV GEMM -- which lets it be produced by that GEMM.
 //
-// Design on CDNA4 (one wavefront = 32 query rows, tiles of 64 keys):
+// Design on CDNA4 (one wavefront = 32 query columns, tiles of KT keys):
 //  * Scores are computed transposed, S^T = K_hat Q_hat^T, with the scaled
-//    FP4 MFMA 32x32x64: A = 32 keys (16-byte rows of K_hat straight from
-//    memory), B = the wave's 32 query rows (loop-invariant registers).  The
+//    FP4 MFMA 32x32x64: A = 32 keys (16 bytes of one K_hat row per lane),
+//    B = the wave's 32 query rows (loop-invariant registers).  The
 //    accumulator gives each lane one query column and 16 keys.
-//  * One v_permlane32_swap per register pair turns the two 32-key S^T blocks
-//    into "lane = (query, 32-key block)": every lane then holds exactly the
-//    32 keys that share one P_hat scale.  Block max, exp, block exponent and
-//    the E2M1 conversion run in-lane; the row max needs one more swap.
-//  * P_hat is then already the B operand of O^T = V_hat^T P_hat^T
-//    (A = 32 channels x 64 keys of the token-blocked V_hat, again one
-//    16-byte load per lane), so the output accumulator is also "lane =
-//    query", and alpha / l never leave their lane.
-//  * P-Reordering: one more MFMA with A = all-ones E2M1 codes adds
-//    rowsum(P_hat) to the running l -- the normalizer is a row of the same
-//    PV product ([V_hat | 1]) instead of a VALU reduction.
+//  * One v_permlane32_swap per register pair turns two 32-key S^T blocks into
+//    "lane = (query, 32-key block)": every lane then holds exactly the 32
+//    keys that share one P_hat scale.  Block max, exp, block exponent and the
+//    E2M1 conversion run in-lane; the row max needs one more swap.
+//  * P_hat is then already the B operand of O^T = V_hat^T P_hat^T (A = 32
+//    channels x 64 keys of V_hat), so the output accumulator is "lane =
+//    query" too: alpha, m and l never leave their lane.
+//  * P-Reordering: one more MFMA with A = all-ones E2M1 codes yields
+//    rowsum(P_hat) -- the normalizer is a row of the same PV product
+//    ([V_hat | 1]) instead of a VALU reduction.
+//  * Prefill: a workgroup is 4 wavefronts that read the same KV head (the
+//    heads of one GQA group, or consecutive row blocks of one head); each
+//    K_hat/V_hat tile is loaded once per workgroup with 1 KB-contiguous
+//    loads and staged through double-buffered LDS in the MFMA operand order
+//    (a lane reads its operand as one conflict-free 16-byte LDS load).  The
+//    grid's fastest dimension is the KV head, so the round-robin dispatch over
+//    the 8 XCDs keeps each KV head's tiles in one L2.
+//  * Split-KV (decode): one wavefront per (b, KV head, chunk) streams its
+//    chunk from HBM with a one-tile register prefetch; an ordered merge
+//    kernel combines the FP16 (m, l) partial states.
 #include "hifa4_device.hpp"
 #include "hifa4_internal.hpp"
 
@@ -32,19 +41,11 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
-struct KvPtrs {
-  const uint8_t* kc;  // K_hat codes of this (b, g), row layout
-  const uint8_t* ks;  // K_hat scales
-  const uint8_t* vc;  // V_hat codes, token layout
-  const uint8_t* vs;  // V_hat scales
-  int64_t npad;       // padded KV length
-};
-
 // Scale word for the S^T MFMA's k-step s: byte 2*(s%2) of word s/2 holds the
 // scale of the 32-channel block (2*s + lane/32).  Built from a row's scale
 // bytes by shifting out the other half's byte.
 template <int D>
-__device__ __forceinline__ void load_row_scales(const uint8_t* row, int hf, uint32_t (&w)[(D / 64 + 1) / 2]) {
+__device__ __forceinline__ void row_scales(const uint8_t* row, int hf, uint32_t (&w)[(D / 64 + 1) / 2]) {
   if constexpr (D == 64) {
     w[0] = (uint32_t)(*reinterpret_cast<const uint16_t*>(row)) >> (8 * hf);
   } else if constexpr (D == 128) {
@@ -56,108 +57,110 @@ __device__ __forceinline__ void load_row_scales(const uint8_t* row, int hf, uint
   }
 }
 
-// One 64-key tile of the online-softmax recurrence for the wave's 32 query
-// columns.  lim: last valid key of this lane's query column.
-template <int D, bool REORDER, bool DUMP>
-__device__ __forceinline__ void attn_tile(const KvPtrs& kv, int kb0, bool need_mask, int lim,
-                                          float c, const uint4 (&qb)[D / 64],
-                                          const uint32_t (&qsc)[(D / 64 + 1) / 2],
-                                          v16f (&accO)[D / 32], v16f& accL, float& m, float& l,
-                                          uint8_t* phat_codes_row, uint8_t* phat_scales_row) {
-  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2;
-  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+// S^T block of a tile: 32 keys x the wave's 32 query columns.
+template <int D>
+__device__ __forceinline__ v16f score_block(const uint4 (&ka)[D / 64], const uint32_t (&ksw)[(D / 64 + 1) / 2],
+                                            const uint4 (&qb)[D / 64], const uint32_t (&qsc)[(D / 64 + 1) / 2]) {
+  v16f acc = zero16();
+#pragma unroll
+  for (int s = 0; s < D / 64; s++) {
+    if (s % 2 == 0)
+      acc = mfma_fp4<0, 0>(ka[s], (int)ksw[s / 2], qb[s], (int)qsc[s / 2], acc);
+    else
+      acc = mfma_fp4<2, 2>(ka[s], (int)ksw[s / 2], qb[s], (int)qsc[s / 2], acc);
+  }
+  return acc;
+}
 
-  // ---- operand loads: K_hat rows (A of S^T) and V_hat channel rows (A of O^T)
-  uint4 ka[2][KS];
-  uint32_t ksw[2][SW];
-#pragma unroll
-  for (int mi = 0; mi < 2; mi++) {
-    const int64_t key = kb0 + 32 * mi + l32;
-    const uint8_t* kr = kv.kc + key * (D / 2);
-#pragma unroll
-    for (int s = 0; s < KS; s++) ka[mi][s] = *reinterpret_cast<const uint4*>(kr + (2 * s + hf) * 16);
-    load_row_scales<D>(kv.ks + key * (D / 32), hf, ksw[mi]);
-  }
-  uint4 va[CT];
-  uint32_t vsw[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ct++) {
-    const int64_t ch = 32 * ct + l32;
-    va[ct] = *reinterpret_cast<const uint4*>(kv.vc + ch * (kv.npad / 2) + kb0 / 2 + 16 * hf);
-    vsw[ct] = kv.vs[ch * (kv.npad / 32) + kb0 / 32 + hf];
-  }
+// The online-softmax step of one tile of KT keys given its S^T blocks:
+// running max, P, P_hat, normalizer, O rescale and O^T += V_hat^T P_hat^T.
+// vops.a(u, ct) / vops.sc(ct) supply the V_hat operands (byte 2u of the scale
+// word is unit u's block).  lim: last valid key of this lane's query column.
+template <int D, int KT, bool REORDER, bool DUMP, class VOps>
+__device__ __forceinline__ void softmax_pv(v16f (&sacc)[KT / 32], int kb0, bool need_mask, int lim,
+                                           float c, const VOps& vops, v16f (&accO)[D / 32],
+                                           float& m, float& l, uint8_t* phat_codes_row,
+                                           uint8_t* phat_scales_row) {
+  constexpr int CT = D / 32, NU = KT / 64;
+  const int hf = (threadIdx.x >> 5) & 1;
 
-  // ---- S^T for keys [kb0, kb0+32) and [kb0+32, kb0+64)
-  v16f s0 = zero16(), s1 = zero16();
+  // lane = (query, 32-key block 2u + hf): X[u][r] is key 8(r/4) + r%4 of the
+  // block, Y[u][r] the key 4 further.
+  float X[NU][16], Y[NU][16];
 #pragma unroll
-  for (int s = 0; s < KS; s++) {
-    if (s % 2 == 0) {
-      s0 = mfma_fp4<0, 0>(ka[0][s], (int)ksw[0][s / 2], qb[s], (int)qsc[s / 2], s0);
-      s1 = mfma_fp4<0, 0>(ka[1][s], (int)ksw[1][s / 2], qb[s], (int)qsc[s / 2], s1);
-    } else {
-      s0 = mfma_fp4<2, 2>(ka[0][s], (int)ksw[0][s / 2], qb[s], (int)qsc[s / 2], s0);
-      s1 = mfma_fp4<2, 2>(ka[1][s], (int)ksw[1][s / 2], qb[s], (int)qsc[s / 2], s1);
-    }
-  }
-
-  // ---- lane = (query l32, 32-key block hf): X[r] is key 8(r/4) + r%4 of the
-  // block, Y[r] the key 4 further.
-  float X[16], Y[16];
-#pragma unroll
-  for (int r = 0; r < 16; r++) {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0[r]), __float_as_uint(s1[r]),
-                                               false, false);
-    X[r] = __uint_as_float(sw[0]);
-    Y[r] = __uint_as_float(sw[1]);
-  }
-  if (need_mask) {
-    const int base = kb0 + 32 * hf;
+  for (int u = 0; u < NU; u++)
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-      const int kx = base + 8 * (r / 4) + (r % 4);
-      if (kx > lim) X[r] = kNegInf;
-      if (kx + 4 > lim) Y[r] = kNegInf;
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sacc[2 * u][r]),
+                                                 __float_as_uint(sacc[2 * u + 1][r]), false, false);
+      X[u][r] = __uint_as_float(sw[0]);
+      Y[u][r] = __uint_as_float(sw[1]);
+    }
+  if (need_mask) {
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      const int base = kb0 + 64 * u + 32 * hf;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int kx = base + 8 * (r / 4) + (r % 4);
+        if (kx > lim) X[u][r] = kNegInf;
+        if (kx + 4 > lim) Y[u][r] = kNegInf;
+      }
     }
   }
 
-  // ---- running max (log2 domain, FP16 state)
-  float bm = kNegInf;
+  // running max (log2 domain, FP16 state)
+  float bm[NU];
+  float rmax = kNegInf;
 #pragma unroll
-  for (int r = 0; r < 16; r++) bm = fmaxf(bm, fmaxf(X[r], Y[r]));
-  const float smax = fmaxf(bm, other_half(bm));
+  for (int u = 0; u < NU; u++) {
+    float x = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; r++) x = fmaxf(x, fmaxf(X[u][r], Y[u][r]));
+    bm[u] = x;
+    rmax = fmaxf(rmax, x);
+  }
+  const float smax = fmaxf(rmax, other_half(rmax));
   const float mt = c * smax;
   const float m_new = round_f16(fmaxf(m, mt));
   const float m_use = (m_new == kNegInf) ? 0.0f : m_new;  // column with no valid key yet
   const float alpha = exp2_hw(m - m_use);
 
-  // ---- P = 2^(S c - m); P_hat block exponent from the block's largest t
+  // P = 2^(S c - m); each block's exponent from its largest t
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    X[r] = exp2_hw(__builtin_fmaf(X[r], c, -m_use));
-    Y[r] = exp2_hw(__builtin_fmaf(Y[r], c, -m_use));
-  }
-  const float tmax = __builtin_fmaf(bm, c, -m_use);
-  const float ef = fminf(fmaxf(floorf(tmax) - 2.0f, -127.0f), 127.0f);
-  const int e = (int)ef;
-  const float psc_f = pow2f(e);
-  uint32_t pw[4];
+  for (int u = 0; u < NU; u++)
 #pragma unroll
-  for (int w = 0; w < 4; w++) {
-    uint32_t x = cvt_fp4x2<0>(0u, X[4 * w], X[4 * w + 1], psc_f);
-    x = cvt_fp4x2<1>(x, X[4 * w + 2], X[4 * w + 3], psc_f);
-    x = cvt_fp4x2<2>(x, Y[4 * w], Y[4 * w + 1], psc_f);
-    pw[w] = cvt_fp4x2<3>(x, Y[4 * w + 2], Y[4 * w + 3], psc_f);
-  }
-  const uint4 ph = {pw[0], pw[1], pw[2], pw[3]};
-  const int psc = e + 127;
-  if constexpr (DUMP) {
-    if (phat_codes_row) {
-      *reinterpret_cast<uint4*>(phat_codes_row + kb0 / 2 + 16 * hf) = ph;
-      phat_scales_row[kb0 / 32 + hf] = (uint8_t)psc;
+    for (int r = 0; r < 16; r++) {
+      X[u][r] = exp2_hw(__builtin_fmaf(X[u][r], c, -m_use));
+      Y[u][r] = exp2_hw(__builtin_fmaf(Y[u][r], c, -m_use));
+    }
+  uint4 ph[NU];
+  int psc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; u++) {
+    const float tmax = __builtin_fmaf(bm[u], c, -m_use);
+    const float ef = fminf(fmaxf(floorf(tmax) - 2.0f, -127.0f), 127.0f);
+    const int e = (int)ef;
+    const float sc = pow2f(e);
+    uint32_t pw[4];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      uint32_t x = cvt_fp4x2<0>(0u, X[u][4 * w], X[u][4 * w + 1], sc);
+      x = cvt_fp4x2<1>(x, X[u][4 * w + 2], X[u][4 * w + 3], sc);
+      x = cvt_fp4x2<2>(x, Y[u][4 * w], Y[u][4 * w + 1], sc);
+      pw[w] = cvt_fp4x2<3>(x, Y[u][4 * w + 2], Y[u][4 * w + 3], sc);
+    }
+    ph[u] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    psc[u] = e + 127;
+    if constexpr (DUMP) {
+      if (phat_codes_row) {
+        *reinterpret_cast<uint4*>(phat_codes_row + kb0 / 2 + 32 * u + 16 * hf) = ph[u];
+        phat_scales_row[kb0 / 32 + 2 * u + hf] = (uint8_t)psc[u];
+      }
     }
   }
 
-  // ---- O <- alpha O (skipped when the max did not move for any column)
+  // O <- alpha O (skipped when the max did not move for any column)
   if (!__all(alpha == 1.0f)) {
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
@@ -165,30 +168,59 @@ __device__ __forceinline__ void attn_tile(const KvPtrs& kv, int kb0, bool need_m
       for (int r = 0; r < 16; r++) accO[ct][r] = accO[ct][r] * alpha;
   }
 
-  // ---- normalizer
+  // normalizer: l = fp16(fp32(alpha l) + rowsum)
+  float rs;
   if constexpr (REORDER) {
-    const float al = alpha * l;
+    // P-Reordering: the row sum of P_hat comes out of the matrix core, as one
+    // more row of the PV product (A = all-ones E2M1 codes, scale 2^0).
+    const uint4 ones = {0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u};
+    v16f sl = mfma_fp4<0, 0>(ones, 127, ph[0], psc[0], zero16());
 #pragma unroll
-    for (int r = 0; r < 16; r++) accL[r] = al;
-    const uint4 ones = {0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u};  // E2M1 1.0
-    accL = mfma_fp4<0, 0>(ones, 127, ph, psc, accL);
-    l = round_f16(accL[0]);
+    for (int u = 1; u < NU; u++) sl = mfma_fp4<0, 0>(ones, 127, ph[u], psc[u], sl);
+    rs = sl[0];
   } else {
-    float rs = 0.0f;
+    rs = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      rs = rs + X[r];
-      rs = rs + Y[r];
-    }
+    for (int u = 0; u < NU; u++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        rs = rs + X[u][r];
+        rs = rs + Y[u][r];
+      }
     rs = rs + other_half(rs);
-    const float al = alpha * l;
-    l = round_f16(al + rs);
   }
+  const float al = alpha * l;
+  l = round_f16(al + rs);
 
-  // ---- O^T += V_hat^T P_hat^T
+  // O^T += V_hat^T P_hat^T
 #pragma unroll
-  for (int ct = 0; ct < CT; ct++) accO[ct] = mfma_fp4<0, 0>(va[ct], (int)vsw[ct], ph, psc, accO[ct]);
+  for (int ct = 0; ct < CT; ct++) {
+    const int vsc = (int)vops.sc(ct);
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      if (u == 0)
+        accO[ct] = mfma_fp4<0, 0>(vops.a(0, ct), vsc, ph[0], psc[0], accO[ct]);
+      else
+        accO[ct] = mfma_fp4<2, 0>(vops.a(u, ct), vsc, ph[u], psc[u], accO[ct]);
+    }
+  }
   m = m_new;
+}
+
+// Epilogue: out = fp16(O / l) for the lane's query row (channels 32ct + 8(r/4) + 4hf + r%4).
+template <int D>
+__device__ __forceinline__ void store_out(uint16_t* orow, const v16f (&accO)[D / 32], float l) {
+  const int hf = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ct++)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; r4++) {
+      uint32_t lo = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 0] / l) |
+                    ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 1] / l) << 16);
+      uint32_t hi = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 2] / l) |
+                    ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 3] / l) << 16);
+      *reinterpret_cast<uint2*>(orow + 32 * ct + 8 * r4 + 4 * hf) = make_uint2(lo, hi);
+    }
 }
 
 struct KParams {
@@ -207,85 +239,220 @@ struct KParams {
   float* ws_ml;
   int64_t B, Hq, Hkv, N_q, N_kv, Npad_q, Npad_kv;
   int G, num_splits, n_tiles, tiles_per_split;
+  int heads_per_wg;  // query heads per prefill workgroup (the rest of its 4 waves are row blocks)
   float c;
 };
 
 // ---------------------------------------------------------------------------
-// Prefill: block = 4 wavefronts = 128 consecutive query rows of one (b, h).
-// Grid (B * Hq, ceil(N_q / 128)); the row blocks run last-first so that the
-// longest causal blocks start earliest.
+// Prefill.  Workgroup = 4 wavefronts on KV head (b, g): nh query heads of the
+// group x (4 / nh) row blocks of 32 rows.  Grid (B * Hkv * G/nh, row groups);
+// row groups run last-first so the longest causal work starts earliest.
+//
+// LDS stage of one tile (KT keys), all in MFMA operand order:
+//   [K_hat codes: KT/32 blocks x D/64 k-steps x 64 lanes x 16 B]
+//   [V_hat codes: KT/64 units x D/32 channel tiles x 64 lanes x 16 B]
+//   [K_hat scales: KT keys x D/32 B][V_hat scales: KT/64 tiles x D x 2 B]
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool REORDER, bool DUMP>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(KParams p) {
-  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / p.Hq, h = bh % p.Hq, g = h / p.G;
-  const int64_t qblk = (int64_t)gridDim.y - 1 - blockIdx.y;
-  const int64_t row0 = qblk * 128 + 32 * wave;
-  if (row0 >= p.N_q) return;
+template <int D, int KT>
+struct Stage {
+  static constexpr int KS = D / 64, CT = D / 32, NB = KT / 32, NU = KT / 64;
+  static constexpr int KC_OFF = 0;
+  static constexpr int VC_OFF = KT * D / 2;
+  static constexpr int KSC_OFF = KT * D;
+  static constexpr int KSC_BYTES = KT * D / 32;
+  static constexpr int VSC_OFF = KSC_OFF + KSC_BYTES;
+  static constexpr int VSC_BYTES = KT * D / 32;
+  static constexpr int BYTES = VSC_OFF + VSC_BYTES;
+  static constexpr int N_KC = NB * KS;   // 1 KB pieces of K_hat codes
+  static constexpr int N_VC = NU * CT;   // 1 KB pieces of V_hat codes
+  // every wave copies CODE_PER_WAVE code pieces and SC_UNITS 16-byte units of
+  // the scale bytes (a quarter of them): the same compile-time work per wave
+  static constexpr int CODE_PER_WAVE = (N_KC + N_VC) / 4;
+  static constexpr int SC_UNITS = (KSC_BYTES + VSC_BYTES) / 16 / 4;
+  static constexpr int PER_WAVE = CODE_PER_WAVE + 1;
+  static_assert((N_KC + N_VC) % 4 == 0, "code pieces split evenly over 4 waves");
+  static_assert(SC_UNITS >= 1 && SC_UNITS <= 64, "scale bytes fit one load per wave");
+};
 
-  // Q_hat rows of this wave: B operand of S^T, resident for the whole loop.
-  const int64_t qrow = row0 + l32;
-  const uint8_t* qr = p.q_codes + (bh * p.Npad_q + qrow) * (D / 2);
-  uint4 qb[KS];
+// The pieces this wave copies: per-lane source pointers for the tile at key 0
+// (a tile at kb0 adds kb0 * step bytes) and LDS destinations.  Lanes beyond a
+// wave's share of the scale bytes repeat its last unit (same bytes to the same
+// LDS address), so every lane runs the same straight-line copy.
+template <int D, int KT>
+struct StagePlan {
+  const uint8_t* src[Stage<D, KT>::PER_WAVE];
+  int dst[Stage<D, KT>::PER_WAVE];
+};
+
+struct KvBases {
+  const uint8_t* kc;  // K_hat codes of (b, g): [Npad][D/2]
+  const uint8_t* ks;  // K_hat scales: [Npad][D/32]
+  const uint8_t* vc;  // V_hat codes: [Npad/64][D][32]
+  const uint8_t* vs;  // V_hat scales: [Npad/64][D][2]
+};
+
+template <int D, int KT>
+__device__ __forceinline__ void make_plan(const KvBases& kv, StagePlan<D, KT>& pl) {
+  using S = Stage<D, KT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
 #pragma unroll
-  for (int s = 0; s < KS; s++) qb[s] = *reinterpret_cast<const uint4*>(qr + (2 * s + hf) * 16);
-  uint32_t qsc[SW];
-  load_row_scales<D>(p.q_scales + (bh * p.Npad_q + qrow) * (D / 32), hf, qsc);
+  for (int j = 0; j < S::CODE_PER_WAVE; j++) {
+    const int i = wave + 4 * j;  // code piece index
+    if (i < S::N_KC) {
+      const int b = i / S::KS, s = i % S::KS;
+      pl.src[j] = kv.kc + (32 * b + l32) * (D / 2) + (2 * s + hf) * 16;
+      pl.dst[j] = S::KC_OFF + i * 1024 + lane * 16;
+    } else {
+      const int jj = i - S::N_KC, u = jj / S::CT, ct = jj % S::CT;
+      pl.src[j] = kv.vc + (u * D + 32 * ct + l32) * 32 + 16 * hf;
+      pl.dst[j] = S::VC_OFF + jj * 1024 + lane * 16;
+    }
+  }
+  const int k = wave * S::SC_UNITS + (lane < S::SC_UNITS ? lane : S::SC_UNITS - 1);
+  const bool kside = k * 16 < S::KSC_BYTES;
+  const int kk = k - S::KSC_BYTES / 16;
+  pl.src[S::CODE_PER_WAVE] = kside ? kv.ks + k * 16 : kv.vs + kk * 16;
+  pl.dst[S::CODE_PER_WAVE] = kside ? S::KSC_OFF + k * 16 : S::VSC_OFF + kk * 16;
+}
 
-  KvPtrs kv;
-  const int64_t bg = b * p.Hkv + g;
+template <int D, int KT>
+__device__ __forceinline__ void stage_load(const StagePlan<D, KT>& pl, int kb0,
+                                           uint4 (&reg)[Stage<D, KT>::PER_WAVE]) {
+  using S = Stage<D, KT>;
+#pragma unroll
+  for (int j = 0; j < S::CODE_PER_WAVE; j++)
+    reg[j] = *reinterpret_cast<const uint4*>(pl.src[j] + (int64_t)kb0 * (D / 2));
+  reg[S::CODE_PER_WAVE] =
+      *reinterpret_cast<const uint4*>(pl.src[S::CODE_PER_WAVE] + (int64_t)kb0 * (D / 32));
+}
+
+template <int D, int KT>
+__device__ __forceinline__ void stage_store(uint8_t* stage, const StagePlan<D, KT>& pl,
+                                            const uint4 (&reg)[Stage<D, KT>::PER_WAVE]) {
+#pragma unroll
+  for (int j = 0; j < Stage<D, KT>::PER_WAVE; j++)
+    *reinterpret_cast<uint4*>(stage + pl.dst[j]) = reg[j];
+}
+
+// V_hat operands read from an LDS stage.
+template <int D, int KT>
+struct LdsV {
+  const uint8_t* st;
+  __device__ __forceinline__ uint4 a(int u, int ct) const {
+    const int lane = threadIdx.x & 63;
+    return *reinterpret_cast<const uint4*>(st + Stage<D, KT>::VC_OFF + (u * (D / 32) + ct) * 1024 + lane * 16);
+  }
+  __device__ __forceinline__ uint32_t sc(int ct) const {
+    const int lane = threadIdx.x & 63, hf = lane >> 5, ch = 32 * ct + (lane & 31);
+    const uint8_t* p = st + Stage<D, KT>::VSC_OFF + ch * 2;
+    uint32_t w = ((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) >> (8 * hf)) & 0xFFu;
+    if constexpr (KT == 128)
+      w |= (((uint32_t)(*reinterpret_cast<const uint16_t*>(p + D * 2)) >> (8 * hf)) & 0xFFu) << 16;
+    return w;
+  }
+};
+
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
+  using S = Stage<D, KT>;
+  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BYTES];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int nh = p.heads_per_wg, nr = 4 / nh;
+  const int64_t chunks = p.G / nh;  // head chunks per KV head
+  const int64_t bgc = blockIdx.x;
+  const int64_t hc = bgc / (p.B * p.Hkv), bg = bgc % (p.B * p.Hkv);
+  const int64_t b = bg / p.Hkv, g = bg % p.Hkv;
+  const int64_t h = g * p.G + hc * nh + (wave % nh);
+  const int64_t rgrp = (int64_t)gridDim.y - 1 - blockIdx.y;
+  const int64_t wg_row0 = rgrp * 32 * nr;
+  const int64_t row0 = wg_row0 + 32 * (wave / nh);
+  const int64_t bh = b * p.Hq + h;
+  (void)chunks;
+
+  KvBases kv;
   kv.kc = p.k_codes + bg * p.Npad_kv * (D / 2);
   kv.ks = p.k_scales + bg * p.Npad_kv * (D / 32);
-  kv.vc = p.v_codes + bg * D * (p.Npad_kv / 2);
-  kv.vs = p.v_scales + bg * D * (p.Npad_kv / 32);
-  kv.npad = p.Npad_kv;
+  kv.vc = p.v_codes + bg * p.Npad_kv * (D / 2);
+  kv.vs = p.v_scales + bg * p.Npad_kv * (D / 32);
 
   const int64_t shift = p.N_kv - p.N_q;  // causal diagonal offset (bottom-right aligned)
-  int lim = (int)(p.N_kv - 1);
-  if (CAUSAL) lim = (int)min64(qrow + shift, p.N_kv - 1);
-  // smallest limit in the wave (its first row) decides when masking is needed
-  const int wave_lim = CAUSAL ? (int)min64(row0 + shift, p.N_kv - 1) : (int)(p.N_kv - 1);
+  const int64_t wg_last_row = min64(wg_row0 + 32 * nr - 1, p.N_q - 1);
+  const int64_t wg_last_key = CAUSAL ? min64(wg_last_row + shift, p.N_kv - 1) : p.N_kv - 1;
+  const int tiles = (int)(wg_last_key / KT) + 1;
+  const bool wave_active = row0 < p.N_q;
   const int64_t last_row = min64(row0 + 31, p.N_q - 1);
-  const int64_t last_key = CAUSAL ? min64(last_row + shift, p.N_kv - 1) : p.N_kv - 1;
-  const int tiles = (int)(last_key / kKvTile) + 1;
+  const int wave_last_key = (int)(CAUSAL ? min64(last_row + shift, p.N_kv - 1) : p.N_kv - 1);
+  const int wave_lim = CAUSAL ? (int)min64(row0 + shift, p.N_kv - 1) : (int)(p.N_kv - 1);
+  const int64_t qrow = row0 + l32;
+  const int lim = CAUSAL ? (int)min64(qrow + shift, p.N_kv - 1) : (int)(p.N_kv - 1);
+
+  // Q_hat rows of this wave: B operand of S^T, resident for the whole loop.
+  uint4 qb[KS];
+  uint32_t qsc[SW];
+  if (wave_active) {
+    const uint8_t* qr = p.q_codes + (bh * p.Npad_q + qrow) * (D / 2);
+#pragma unroll
+    for (int s = 0; s < KS; s++) qb[s] = *reinterpret_cast<const uint4*>(qr + (2 * s + hf) * 16);
+    row_scales<D>(p.q_scales + (bh * p.Npad_q + qrow) * (D / 32), hf, qsc);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; s++) qb[s] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int w = 0; w < SW; w++) qsc[w] = 0;
+  }
 
   uint8_t* phc = nullptr;
   uint8_t* phs = nullptr;
   if constexpr (DUMP) {
-    if (qrow < p.N_q) {
+    if (wave_active && qrow < p.N_q) {
       phc = p.phat_codes + (bh * p.N_q + qrow) * (p.Npad_kv / 2);
       phs = p.phat_scales + (bh * p.N_q + qrow) * (p.Npad_kv / 32);
     }
   }
 
+  StagePlan<D, KT> plan;
+  make_plan<D, KT>(kv, plan);
+  uint4 stage_reg[S::PER_WAVE];
+  stage_load<D, KT>(plan, 0, stage_reg);
+  stage_store<D, KT>(smem, plan, stage_reg);
+  __syncthreads();
+
   v16f accO[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
-  v16f accL = zero16();
   float m = kNegInf, l = 0.0f;
   for (int t = 0; t < tiles; t++) {
-    const int kb0 = t * kKvTile;
-    const bool need_mask = (kb0 + kKvTile - 1) > wave_lim;
-    attn_tile<D, REORDER, DUMP>(kv, kb0, need_mask, lim, p.c, qb, qsc, accO, accL, m, l, phc, phs);
+    const int kb0 = t * KT;
+    // copy the next tile into the other stage while this one is computed; the
+    // last iteration re-copies its own tile (in bounds; that stage is not read again)
+    const int next_kb0 = (t + 1 < tiles) ? kb0 + KT : kb0;
+    stage_load<D, KT>(plan, next_kb0, stage_reg);
+    const uint8_t* st = smem + (t & 1) * S::BYTES;
+    if (wave_active && kb0 <= wave_last_key) {
+      v16f sacc[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; bb++) {
+        uint4 ka[KS];
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+          ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
+        uint32_t ksw[SW];
+        row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
+        sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
+      }
+      const bool need_mask = (kb0 + KT - 1) > wave_lim;
+      LdsV<D, KT> vops{st};
+      softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
+    }
+    stage_store<D, KT>(smem + ((t + 1) & 1) * S::BYTES, plan, stage_reg);
+    __syncthreads();
   }
 
-  // ---- out = fp16(O / l): lane holds channels 32ct + 8(r/4) + 4hf + r%4
-  if (qrow < p.N_q) {
-    uint16_t* orow = p.out + (bh * p.N_q + qrow) * D;
-#pragma unroll
-    for (int ct = 0; ct < CT; ct++) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; r4++) {
-        uint32_t lo = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 0] / l) |
-                      ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 1] / l) << 16);
-        uint32_t hi = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 2] / l) |
-                      ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 3] / l) << 16);
-        *reinterpret_cast<uint2*>(orow + 32 * ct + 8 * r4 + 4 * hf) = make_uint2(lo, hi);
-      }
-    }
-  }
+  if (wave_active && qrow < p.N_q) store_out<D>(p.out + (bh * p.N_q + qrow) * D, accO, l);
 }
 
 // ---------------------------------------------------------------------------
@@ -294,9 +461,53 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(KParams p) {
 // zero padding).  Q is smoothed and quantized in-kernel from binary16 (or
 // read pre-quantized).  Each chunk writes its (m, l, O) partial state.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
+
+// K_hat / V_hat operands of one tile held in registers (split-KV path).
+template <int D, int KT>
+struct RegOps {
+  static constexpr int KS = D / 64, CT = D / 32, NB = KT / 32, NU = KT / 64, SW = (KS + 1) / 2;
+  uint4 ka[NB][KS];
+  uint32_t ksw[NB][SW];
+  uint4 va[NU][CT];
+  uint32_t vsw[CT];
+  __device__ __forceinline__ uint4 a(int u, int ct) const { return va[u][ct]; }
+  __device__ __forceinline__ uint32_t sc(int ct) const { return vsw[ct]; }
+};
+
+template <int D, int KT>
+__device__ __forceinline__ void reg_load_k(const KvBases& kv, int kb0, RegOps<D, KT>& op) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int bb = 0; bb < KT / 32; bb++) {
+    const int64_t key = kb0 + 32 * bb + l32;
+    const uint8_t* kr = kv.kc + key * (D / 2);
+#pragma unroll
+    for (int s = 0; s < D / 64; s++) op.ka[bb][s] = *reinterpret_cast<const uint4*>(kr + (2 * s + hf) * 16);
+    row_scales<D>(kv.ks + key * (D / 32), hf, op.ksw[bb]);
+  }
+}
+
+template <int D, int KT>
+__device__ __forceinline__ void reg_load_v(const KvBases& kv, int kb0, RegOps<D, KT>& op) {
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ct++) {
+    const int64_t ch = 32 * ct + l32;
+    uint32_t w = 0;
+#pragma unroll
+    for (int u = 0; u < KT / 64; u++) {
+      const int64_t tile = kb0 / 64 + u;
+      op.va[u][ct] = *reinterpret_cast<const uint4*>(kv.vc + (tile * D + ch) * 32 + 16 * hf);
+      const uint32_t sb = (uint32_t)(*reinterpret_cast<const uint16_t*>(kv.vs + (tile * D + ch) * 2)) >> (8 * hf);
+      w |= (sb & 0xFFu) << (16 * u);
+    }
+    op.vsw[ct] = w;
+  }
+}
+
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
 __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
-  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2;
+  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
   const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t total = p.B * p.Hkv * p.num_splits;
@@ -358,18 +569,16 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
     const int64_t qr_idx = (b * p.Hq + h) * p.Npad_q + i;
     const uint8_t* qr = p.q_codes + qr_idx * (D / 2);
 #pragma unroll
-    for (int s = 0; s < KS; s++) {
+    for (int s = 0; s < KS; s++)
       qb[s] = real ? *reinterpret_cast<const uint4*>(qr + (2 * s + hf) * 16) : make_uint4(0, 0, 0, 0);
-    }
-    if (real) load_row_scales<D>(p.q_scales + qr_idx * (D / 32), hf, qsc);
+    if (real) row_scales<D>(p.q_scales + qr_idx * (D / 32), hf, qsc);
   }
 
-  KvPtrs kv;
+  KvBases kv;
   kv.kc = p.k_codes + bg * p.Npad_kv * (D / 2);
   kv.ks = p.k_scales + bg * p.Npad_kv * (D / 32);
-  kv.vc = p.v_codes + bg * D * (p.Npad_kv / 2);
-  kv.vs = p.v_scales + bg * D * (p.Npad_kv / 32);
-  kv.npad = p.Npad_kv;
+  kv.vc = p.v_codes + bg * p.Npad_kv * (D / 2);
+  kv.vs = p.v_scales + bg * p.Npad_kv * (D / 32);
 
   const int64_t shift = p.N_kv - p.N_q;
   const int lim = CAUSAL ? (int)min64(i + shift, p.N_kv - 1) : (int)(p.N_kv - 1);
@@ -387,29 +596,28 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
   v16f accO[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
-  v16f accL = zero16();
   float m = kNegInf, l = 0.0f;
   const int t0 = chunk * p.tiles_per_split;
   const int t1 = p.n_tiles < t0 + p.tiles_per_split ? p.n_tiles : t0 + p.tiles_per_split;
-  for (int t = t0; t < t1; t++) {
-    const int kb0 = t * kKvTile;
-    const bool need_mask = (kb0 + kKvTile - 1) > wave_lim;
-    attn_tile<D, REORDER, DUMP>(kv, kb0, need_mask, lim, p.c, qb, qsc, accO, accL, m, l, phc, phs);
+  if (t0 < t1) {
+    RegOps<D, KT> op;
+    reg_load_k<D, KT>(kv, t0 * KT, op);
+    reg_load_v<D, KT>(kv, t0 * KT, op);
+    for (int t = t0; t < t1; t++) {
+      const int kb0 = t * KT;
+      const bool more = t + 1 < t1;
+      v16f sacc[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(op.ka[bb], op.ksw[bb], qb, qsc);
+      if (more) reg_load_k<D, KT>(kv, kb0 + KT, op);
+      const bool need_mask = (kb0 + KT - 1) > wave_lim;
+      softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, op, accO, m, l, phc, phs);
+      if (more) reg_load_v<D, KT>(kv, kb0 + KT, op);
+    }
   }
 
   if (real && p.num_splits == 1) {
-    // a single chunk is the whole pass: out = fp16(O / l) directly
-    uint16_t* orow = p.out + row * D;
-#pragma unroll
-    for (int ct = 0; ct < CT; ct++)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; r4++) {
-        uint32_t lo = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 0] / l) |
-                      ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 1] / l) << 16);
-        uint32_t hi = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 2] / l) |
-                      ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 3] / l) << 16);
-        *reinterpret_cast<uint2*>(orow + 32 * ct + 8 * r4 + 4 * hf) = make_uint2(lo, hi);
-      }
+    store_out<D>(p.out + row * D, accO, l);  // a single chunk is the whole pass
   } else if (real) {
     float* wo = p.ws_o + (row * p.num_splits + chunk) * D;
 #pragma unroll
@@ -457,18 +665,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   out[t] = float_to_half_bits(A / lf);
 }
 
-template <int D, bool CAUSAL, bool REORDER, bool DUMP>
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
-  dim3 grid((unsigned)(kp.B * kp.Hq), (unsigned)((kp.N_q + 127) / 128));
-  attn_prefill_kernel<D, CAUSAL, REORDER, DUMP><<<grid, dim3(256), 0, stream>>>(kp);
+  const int nh = kp.heads_per_wg, nr = 4 / nh;
+  // x = (head chunk, b, g) with the KV head fastest: consecutive workgroups
+  // land on consecutive XCDs, so each XCD's L2 serves a fixed set of KV heads
+  dim3 grid((unsigned)(kp.B * kp.Hkv * (kp.G / nh)), (unsigned)((kp.N_q + 32 * nr - 1) / (32 * nr)));
+  attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP><<<grid, dim3(256), 0, stream>>>(kp);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
 hipError_t launch_split_t(const KParams& kp, hipStream_t stream) {
   const int64_t waves = kp.B * kp.Hkv * kp.num_splits;
   dim3 grid((unsigned)((waves + 3) / 4));
-  attn_split_kernel<D, CAUSAL, REORDER, DUMP, QRAW><<<grid, dim3(256), 0, stream>>>(kp);
+  attn_split_kernel<D, KT, CAUSAL, REORDER, DUMP, QRAW><<<grid, dim3(256), 0, stream>>>(kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || kp.num_splits == 1) return e;
   const int64_t rows = kp.B * kp.Hq * kp.N_q;
@@ -502,47 +713,64 @@ KParams make_params(const AttnLaunch& a) {
   kp.Npad_kv = a.Npad_kv;
   kp.G = (int)(a.Hq / a.Hkv);
   kp.num_splits = a.num_splits;
-  kp.n_tiles = (int)((a.N_kv + kKvTile - 1) / kKvTile);
+  kp.n_tiles = (int)((a.N_kv + a.kv_tile - 1) / a.kv_tile);
   kp.tiles_per_split = (kp.n_tiles + a.num_splits - 1) / a.num_splits;
+  kp.heads_per_wg = (kp.G % 4 == 0) ? 4 : (kp.G % 2 == 0) ? 2 : 1;
   kp.c = (float)(1.4426950408889634073599246810019 / __builtin_sqrt((double)a.d));
   return kp;
 }
 
-template <int D>
+template <int D, int KT>
 hipError_t dispatch_prefill(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
   const bool dump = a.phat_codes != nullptr;
   const int key = (a.causal ? 4 : 0) | (a.reorder ? 2 : 0) | (dump ? 1 : 0);
   switch (key) {
-    case 0: return launch_prefill_t<D, false, false, false>(kp, st);
-    case 1: return launch_prefill_t<D, false, false, true>(kp, st);
-    case 2: return launch_prefill_t<D, false, true, false>(kp, st);
-    case 3: return launch_prefill_t<D, false, true, true>(kp, st);
-    case 4: return launch_prefill_t<D, true, false, false>(kp, st);
-    case 5: return launch_prefill_t<D, true, false, true>(kp, st);
-    case 6: return launch_prefill_t<D, true, true, false>(kp, st);
-    default: return launch_prefill_t<D, true, true, true>(kp, st);
+    case 0: return launch_prefill_t<D, KT, false, false, false>(kp, st);
+    case 1: return launch_prefill_t<D, KT, false, false, true>(kp, st);
+    case 2: return launch_prefill_t<D, KT, false, true, false>(kp, st);
+    case 3: return launch_prefill_t<D, KT, false, true, true>(kp, st);
+    case 4: return launch_prefill_t<D, KT, true, false, false>(kp, st);
+    case 5: return launch_prefill_t<D, KT, true, false, true>(kp, st);
+    case 6: return launch_prefill_t<D, KT, true, true, false>(kp, st);
+    default: return launch_prefill_t<D, KT, true, true, true>(kp, st);
   }
 }
 
-template <int D, bool QRAW>
+template <int D, int KT, bool QRAW>
 hipError_t dispatch_split_q(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
   const bool dump = a.phat_codes != nullptr;
   const int key = (a.causal ? 4 : 0) | (a.reorder ? 2 : 0) | (dump ? 1 : 0);
   switch (key) {
-    case 0: return launch_split_t<D, false, false, false, QRAW>(kp, st);
-    case 1: return launch_split_t<D, false, false, true, QRAW>(kp, st);
-    case 2: return launch_split_t<D, false, true, false, QRAW>(kp, st);
-    case 3: return launch_split_t<D, false, true, true, QRAW>(kp, st);
-    case 4: return launch_split_t<D, true, false, false, QRAW>(kp, st);
-    case 5: return launch_split_t<D, true, false, true, QRAW>(kp, st);
-    case 6: return launch_split_t<D, true, true, false, QRAW>(kp, st);
-    default: return launch_split_t<D, true, true, true, QRAW>(kp, st);
+    case 0: return launch_split_t<D, KT, false, false, false, QRAW>(kp, st);
+    case 1: return launch_split_t<D, KT, false, false, true, QRAW>(kp, st);
+    case 2: return launch_split_t<D, KT, false, true, false, QRAW>(kp, st);
+    case 3: return launch_split_t<D, KT, false, true, true, QRAW>(kp, st);
+    case 4: return launch_split_t<D, KT, true, false, false, QRAW>(kp, st);
+    case 5: return launch_split_t<D, KT, true, false, true, QRAW>(kp, st);
+    case 6: return launch_split_t<D, KT, true, true, false, QRAW>(kp, st);
+    default: return launch_split_t<D, KT, true, true, true, QRAW>(kp, st);
   }
 }
 
-template <int D>
+template <int D, int KT>
 hipError_t dispatch_split(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
-  return a.q_f16 ? dispatch_split_q<D, true>(a, kp, st) : dispatch_split_q<D, false>(a, kp, st);
+  return a.q_f16 ? dispatch_split_q<D, KT, true>(a, kp, st) : dispatch_split_q<D, KT, false>(a, kp, st);
+}
+
+template <int D>
+hipError_t dispatch_prefill_kt(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
+  if constexpr (D <= 128) {
+    if (a.kv_tile == 128) return dispatch_prefill<D, 128>(a, kp, st);
+  }
+  return dispatch_prefill<D, 64>(a, kp, st);
+}
+
+template <int D>
+hipError_t dispatch_split_kt(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
+  if constexpr (D <= 128) {
+    if (a.kv_tile == 128) return dispatch_split<D, 128>(a, kp, st);
+  }
+  return dispatch_split<D, 64>(a, kp, st);
 }
 
 }  // namespace
@@ -550,18 +778,18 @@ hipError_t dispatch_split(const AttnLaunch& a, const KParams& kp, hipStream_t st
 hipError_t launch_attn_prefill(const AttnLaunch& a, hipStream_t stream) {
   const KParams kp = make_params(a);
   switch (a.d) {
-    case 64: return dispatch_prefill<64>(a, kp, stream);
-    case 128: return dispatch_prefill<128>(a, kp, stream);
-    default: return dispatch_prefill<256>(a, kp, stream);
+    case 64: return dispatch_prefill_kt<64>(a, kp, stream);
+    case 128: return dispatch_prefill_kt<128>(a, kp, stream);
+    default: return dispatch_prefill_kt<256>(a, kp, stream);
   }
 }
 
 hipError_t launch_attn_split(const AttnLaunch& a, hipStream_t stream) {
   const KParams kp = make_params(a);
   switch (a.d) {
-    case 64: return dispatch_split<64>(a, kp, stream);
-    case 128: return dispatch_split<128>(a, kp, stream);
-    default: return dispatch_split<256>(a, kp, stream);
+    case 64: return dispatch_split_kt<64>(a, kp, stream);
+    case 128: return dispatch_split_kt<128>(a, kp, stream);
+    default: return dispatch_split_kt<256>(a, kp, stream);
   }
 }
 

@@ -6,7 +6,7 @@
 namespace hifa4 {
 
 constexpr int64_t kTokenPad = 128;  // HIFA4_TOKEN_PAD
-constexpr int kKvTile = 64;         // keys per tile (two 32-key S^T MFMA column blocks)
+constexpr int kKvTile = 64;         // default keys per tile (two 32-key S^T MFMA column blocks)
 constexpr int kRowsPerWave = 32;    // query rows (MFMA columns) per wavefront
 constexpr int kWavesPerBlock = 4;
 
@@ -38,7 +38,7 @@ struct AttnLaunch {
   float* ws_ml;  // [rows][C][2] split partial (m, l)
   int64_t B, Hq, Hkv, N_q, N_kv, d;
   int64_t Npad_q, Npad_kv;
-  int causal, smooth, reorder, num_splits;
+  int causal, smooth, reorder, num_splits, kv_tile;
 };
 
 hipError_t launch_attn_prefill(const AttnLaunch& a, hipStream_t stream);

@@ -81,10 +81,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// V along tokens.  One thread per (4 channels, 32-token block): it reads the
-// block's 32 token rows as 8-byte pieces (neighbouring threads read
-// neighbouring channels of the same token, so loads coalesce) and writes one
-// 16-byte code block + one scale byte per channel.  Tokens >= N count as 0.
+// V along tokens, written in the tiled token layout: for each 64-token tile,
+// each channel's 32 code bytes (tokens 64t..64t+63, two 32-token blocks) are
+// contiguous, channels one after another: codes [B][H][Npad/64][d][32],
+// scales [B][H][Npad/64][d][2].  One thread per (4 channels, 32-token block):
+// it reads the block's 32 token rows as 8-byte pieces (neighbouring threads
+// read neighbouring channels of the same token, so loads coalesce) and writes
+// one 16-byte code block + one scale byte per channel.  Tokens >= N count as 0.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, int64_t N,
                                                       int64_t Npad, int64_t d,
@@ -111,6 +114,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
       x[0][i] = x[1][i] = x[2][i] = x[3][i] = 0.0f;
     }
   }
+  const int64_t tile = bh * (Npad / 64) + beta / 2;
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     float amax = 0.0f;
@@ -123,9 +127,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     out.y = pack8_fp4(&x[c][8], sc);
     out.z = pack8_fp4(&x[c][16], sc);
     out.w = pack8_fp4(&x[c][24], sc);
-    const int64_t ch_row = bh * d + cg * 4 + c;
-    *reinterpret_cast<uint4*>(codes + ch_row * (Npad / 2) + beta * 16) = out;
-    scales[ch_row * (Npad / 32) + beta] = (uint8_t)(e + 127);
+    const int64_t ch = tile * d + cg * 4 + c;
+    *reinterpret_cast<uint4*>(codes + ch * 32 + (beta % 2) * 16) = out;
+    scales[ch * 2 + (beta % 2)] = (uint8_t)(e + 127);
   }
 }
 

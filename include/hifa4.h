@@ -28,12 +28,15 @@
  *   with scale byte 0):
  *     row layout (Q, K):   codes [B][H][Npad][d/2],  scales [B][H][Npad][d/32]
  *                          (blocks of 32 consecutive channels of one token)
- *     token layout (V):    codes [B][H][d][Npad/2],  scales [B][H][d][Npad/32]
- *                          (blocks of 32 consecutive tokens of one channel)
+ *     tiled token layout (V): codes [B][H][Npad/64][d][32], scales
+ *                          [B][H][Npad/64][d][2]: blocks of 32 consecutive
+ *                          tokens of one channel; per 64-token tile, each
+ *                          channel's two blocks (32 code bytes, 2 scale bytes)
+ *                          are contiguous, channel after channel.
  * - Errors: argument checks run first, on the host, and touch no device:
  *   HIFA4_EINVAL (bad sizes, NULL where a buffer is required, misaligned
  *   pointers), HIFA4_EUNSUPPORTED (valid but not built: d not 64/128/256,
- *   kv_tile other than 64).  Then HIFA4_ENODEV if no HIP device is visible,
+ *   kv_tile other than 64, or 128 with d <= 128).  Then HIFA4_ENODEV if no HIP device is visible,
  *   HIFA4_EINVAL for a pointer that is not device memory, HIFA4_ENOSPACE for a
  *   too-small workspace, HIFA4_EHIP if a launch fails.  hifa4_last_error()
  *   returns a thread-local message for the last failing call.  No C++
@@ -69,7 +72,7 @@ const char* hifa4_last_error(void);
 
 /*
  * Bytes of one 4-bit tensor in the row layout (v_layout = 0, Q and K) or the
- * token layout (v_layout = 1, V), for B x H x N tokens of d channels.
+ * tiled token layout (v_layout = 1, V), for B x H x N tokens of d channels.
  * EINVAL for negative sizes or d not a multiple of 32.  Host only.
  */
 hifa4_status hifa4_mx4_bytes(int v_layout, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -104,7 +107,7 @@ hifa4_status hifa4_calibrate_smooth(const void* q_cal_f16, const void* k_cal_f16
  * Any of q_f16 / k_f16 / v_f16 may be NULL to skip that tensor (its output
  * pointers are then ignored).  s and inv_s are [Hkv][d] fp32, ignored when
  * smooth = 0.  Codes/scales buffers must hold hifa4_mx4_bytes(...) bytes and
- * be 16-byte aligned (codes) / 4-byte aligned (scales).  Asynchronous.
+ * be 16-byte aligned.  Asynchronous.
  */
 hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void* v_f16,
                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
@@ -122,7 +125,7 @@ typedef struct {
    * and quantized inside the kernel exactly as hifa4_quantize_qkv would. */
   const void* q_f16;
   const float* s;
-  /* K row layout, V token layout (from hifa4_quantize_qkv). */
+  /* K row layout, V tiled token layout (from hifa4_quantize_qkv). */
   const uint8_t* k_codes;
   const uint8_t* k_scales;
   const uint8_t* v_codes;
@@ -132,8 +135,8 @@ typedef struct {
   /* Scratch for split-KV partial states; hifa4_attn_workspace_bytes(). */
   void* workspace;
   size_t workspace_bytes;
-  /* Keys per tile (the tile partition fixes the FP16 state's rounding
-   * sequence).  0 selects the default, 64. */
+  /* Keys per tile: 64, or 128 when d <= 128 (the tile partition fixes the
+   * FP16 state's rounding sequence).  0 selects the default, 64. */
   int kv_tile;
   /* Split-KV: 1 = one pass; C > 1 deals the ceil(N_kv/kv_tile) tiles to C
    * chunks of consecutive tiles, each run from (-inf, 0, 0) and merged in

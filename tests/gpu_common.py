@@ -55,3 +55,19 @@ def oracle_quant(w, s=None, inv=None):
 def mx4_to_dev(pair):
     import bit_flashattention_amd as hf
     return hf.MX4(to_dev(pair[0]), to_dev(pair[1]))
+
+
+def tile_v(pair):
+    """Canonical V_hat ([B][H][d][Npad/2] codes, [B][H][d][Npad/32] scales) -> the
+    library's tiled token layout ([B][H][Npad/64][d][32], [B][H][Npad/64][d][2]).
+    A pure re-arrangement of bytes: no value changes."""
+    codes, scales = pair
+    B, H, d, nb = codes.shape
+    t = nb // 32
+    c = np.ascontiguousarray(codes.reshape(B, H, d, t, 32).transpose(0, 1, 3, 2, 4))
+    s = np.ascontiguousarray(scales.reshape(B, H, d, t, 2).transpose(0, 1, 3, 2, 4))
+    return c, s
+
+
+def v_to_dev(pair):
+    return mx4_to_dev(tile_v(pair))

@@ -12,7 +12,7 @@ import pytest
 import oracle
 import synth
 from gpu_common import (CODE_MATCH, ERR_MAX, ERR_MEAN, code_match_fraction, codes_equal,
-                        mx4_to_dev, oracle_quant, out_error, to_dev, to_host)
+                        mx4_to_dev, oracle_quant, out_error, tile_v, to_dev, to_host, v_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_calibrate_and_quantize_match_oracle(hf, name, kw):
                                  smooth=w.smooth, s=s, inv_s=inv)
     _sync()
     rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
-    for got, ref in ((q4, rq), (k4, rk), (v4, rv)):
+    for got, ref in ((q4, rq), (k4, rk), (v4, tile_v(rv))):
         assert np.all(codes_equal(to_host(got.codes), ref[0]))
         assert np.array_equal(to_host(got.scales), ref[1])
 
@@ -91,7 +91,7 @@ def test_quantize_edge_values(hf):
     v = x.copy()
     _, _, v4 = hf.quantize_qkv(None, None, to_dev(v), Hkv=2)
     _sync()
-    rv = oracle.quantize_v(v)
+    rv = tile_v(oracle.quantize_v(v))
     assert np.all(codes_equal(to_host(v4.codes), rv[0]))
     assert np.array_equal(to_host(v4.scales), rv[1])
 
@@ -101,47 +101,53 @@ def test_quantize_edge_values(hf):
 # ---------------------------------------------------------------------------
 
 ATTN_CASES = [
-    # name, overrides, reorder
-    ("single_head", dict(), 1),
-    ("single_head", dict(), 0),
-    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 1),
-    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 0),
-    ("qwen3_8b", dict(B=1, Hq=2, Hkv=2, N=200, N_kv=330, d=128, n_cal=64), 1),  # ragged, N_q < N_kv
-    ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=384, d=256, n_cal=128), 1),
-    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 1),
-    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 0),
-    ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1),
+    # name, overrides, reorder, kv_tile
+    ("single_head", dict(), 1, 64),
+    ("single_head", dict(), 0, 64),
+    ("single_head", dict(), 1, 128),
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 1, 64),
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 0, 64),
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 1, 128),
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=1, N=512, d=128, n_cal=128), 0, 128),
+    ("qwen3_8b", dict(B=1, Hq=2, Hkv=2, N=200, N_kv=330, d=128, n_cal=64), 1, 64),  # ragged
+    ("qwen3_8b", dict(B=1, Hq=2, Hkv=2, N=200, N_kv=330, d=128, n_cal=64), 1, 128),
+    ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=384, d=256, n_cal=128), 1, 64),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 1, 64),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 0, 128),
+    ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1, 64),
+    ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 0, 128),
 ]
 
 
-def _prefill_case(hf, w, reorder, dump=True):
+def _prefill_case(hf, w, reorder, dump=True, kv_tile=64):
     import torch
     if w.smooth:
         s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
     else:
         s_ref = inv_ref = None
     rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
-    q4, k4, v4 = mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv)
+    q4, k4, v4 = mx4_to_dev(rq), mx4_to_dev(rk), v_to_dev(rv)
     phat = None
     npk = oracle.padded(w.N_kv)
     if dump:
         phat = hf.MX4(torch.zeros((w.B, w.Hq, w.N_q, npk // 2), dtype=torch.uint8, device="cuda"),
                       torch.zeros((w.B, w.Hq, w.N_q, npk // 32), dtype=torch.uint8, device="cuda"))
     out = hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
-                      causal=w.causal, smooth=w.smooth, reorder=reorder, phat=phat)
+                      causal=w.causal, smooth=w.smooth, reorder=reorder, phat=phat,
+                      kv_tile=kv_tile)
     _sync()
     ref = oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=reorder,
-                      kv_tile=64, q4=rq, k4=rk, v4=rv, want_phat=dump)
+                      kv_tile=kv_tile, q4=rq, k4=rk, v4=rv, want_phat=dump)
     return out, phat, ref
 
 
-@pytest.mark.parametrize("name,kw,reorder", ATTN_CASES)
-def test_prefill_matches_oracle(hf, name, kw, reorder):
-    print(f"[prefill] {name} {kw} reorder={reorder}", flush=True)
+@pytest.mark.parametrize("name,kw,reorder,kv_tile", ATTN_CASES)
+def test_prefill_matches_oracle(hf, name, kw, reorder, kv_tile):
+    print(f"[prefill] {name} {kw} reorder={reorder} kv_tile={kv_tile}", flush=True)
     w = synth.WORKLOADS[name](**kw)
     if name == "single_head":
         w.causal = False
-    out, phat, ref = _prefill_case(hf, w, reorder)
+    out, phat, ref = _prefill_case(hf, w, reorder, kv_tile=kv_tile)
     got = to_host(out).reshape(-1, w.d).view(np.uint16)
     frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
     sc = np.mean(to_host(phat.scales).reshape(len(got), -1) == ref["phat_scales"])
@@ -170,10 +176,11 @@ def test_v_ones_gives_one(hf):
 
 
 DECODE_CASES = [
-    dict(B=2, Hq=8, Hkv=2, N_kv=1000, d=128, num_splits=4),
-    dict(B=3, Hq=32, Hkv=8, N_kv=512, d=128, num_splits=1),
-    dict(B=2, Hq=4, Hkv=4, N_kv=700, d=64, num_splits=3),
-    dict(B=1, Hq=8, Hkv=1, N_kv=4096, d=256, num_splits=16),
+    dict(B=2, Hq=8, Hkv=2, N_kv=1000, d=128, num_splits=4, kv_tile=64),
+    dict(B=2, Hq=8, Hkv=2, N_kv=1000, d=128, num_splits=4, kv_tile=128),
+    dict(B=3, Hq=32, Hkv=8, N_kv=512, d=128, num_splits=1, kv_tile=64),
+    dict(B=2, Hq=4, Hkv=4, N_kv=700, d=64, num_splits=3, kv_tile=64),
+    dict(B=1, Hq=8, Hkv=1, N_kv=4096, d=256, num_splits=16, kv_tile=64),
 ]
 
 
@@ -183,6 +190,7 @@ def test_decode_split_matches_oracle(hf, kw):
     print(f"[decode] {kw}", flush=True)
     kw = dict(kw)
     C = kw.pop("num_splits")
+    kt = kw.pop("kv_tile")
     w = synth.decode(n_cal=128, **kw)
     s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
     rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
@@ -191,12 +199,12 @@ def test_decode_split_matches_oracle(hf, kw):
     npk = oracle.padded(w.N_kv)
     phat = hf.MX4(torch.zeros((w.B, w.Hq, 1, npk // 2), dtype=torch.uint8, device="cuda"),
                   torch.zeros((w.B, w.Hq, 1, npk // 32), dtype=torch.uint8, device="cuda"))
-    out = hf.attn_fwd(None, mx4_to_dev(rk), mx4_to_dev(rv), B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=1,
+    out = hf.attn_fwd(None, mx4_to_dev(rk), v_to_dev(rv), B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=1,
                       N_kv=w.N_kv, d=w.d, causal=False, smooth=True, reorder=True,
-                      q_f16=to_dev(w.q), s=to_dev(s_ref), num_splits=C, phat=phat)
+                      q_f16=to_dev(w.q), s=to_dev(s_ref), num_splits=C, phat=phat, kv_tile=kt)
     _sync()
     ref = oracle.attn(w.B, w.Hq, w.Hkv, 1, w.N_kv, w.d, causal=False, reorder=1, num_splits=C,
-                      q4=rq, k4=rk, v4=rv, want_phat=True)
+                      kv_tile=kt, q4=rq, k4=rk, v4=rv, want_phat=True)
     got = to_host(out).reshape(-1, w.d)
     frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
     emax, emean = out_error(got, ref["out"].view(np.float16))
@@ -210,7 +218,7 @@ def test_split_path_with_prequantized_q_and_causal(hf):
     w = synth.qwen3_8b(B=2, Hq=8, Hkv=2, N=4, N_kv=700, d=128, n_cal=64)
     s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
     rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
-    out = hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv), B=2, Hq=8, Hkv=2, N_q=4,
+    out = hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), v_to_dev(rv), B=2, Hq=8, Hkv=2, N_q=4,
                       N_kv=700, d=128, causal=True, smooth=True, reorder=False, num_splits=5)
     _sync()
     ref = oracle.attn(2, 8, 2, 4, 700, 128, causal=True, reorder=0, num_splits=5, q4=rq, k4=rk,
@@ -223,13 +231,13 @@ def test_empty_and_single_key(hf):
     import torch
     w = synth.qwen3_8b(B=1, Hq=2, Hkv=1, N=3, N_kv=1, d=128, n_cal=32)
     rq, rk, rv = oracle_quant(w)
-    out = hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=3,
+    out = hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), v_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=3,
                       N_kv=1, d=128, causal=False, smooth=False, reorder=True)
     _sync()
     ref = oracle.attn(1, 2, 1, 3, 1, 128, causal=False, reorder=1, q4=rq, k4=rk, v4=rv)
     assert np.array_equal(to_host(out).reshape(-1, 128).view(np.uint16), ref["out"])
     # N_q = 0: a successful no-op
     empty = torch.empty((1, 2, 0, 128), dtype=torch.float16, device="cuda")
-    hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), mx4_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=0,
+    hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), v_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=0,
                 N_kv=1, d=128, causal=False, smooth=False, reorder=True, out=empty)
     _sync()
