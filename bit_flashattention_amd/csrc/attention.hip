@@ -319,21 +319,21 @@ __device__ __forceinline__ void make_plan(const KvBases& kv, StagePlan<D, KT>& p
 
 template <int D, int KT>
 __device__ __forceinline__ void stage_load(const StagePlan<D, KT>& pl, int kb0,
-                                           uint4 (&reg)[Stage<D, KT>::PER_WAVE]) {
+                                           u32x4 (&reg)[Stage<D, KT>::PER_WAVE]) {
   using S = Stage<D, KT>;
 #pragma unroll
   for (int j = 0; j < S::CODE_PER_WAVE; j++)
-    reg[j] = *reinterpret_cast<const uint4*>(pl.src[j] + (int64_t)kb0 * (D / 2));
+    reg[j] = *reinterpret_cast<const u32x4*>(pl.src[j] + (int64_t)kb0 * (D / 2));
   reg[S::CODE_PER_WAVE] =
-      *reinterpret_cast<const uint4*>(pl.src[S::CODE_PER_WAVE] + (int64_t)kb0 * (D / 32));
+      *reinterpret_cast<const u32x4*>(pl.src[S::CODE_PER_WAVE] + (int64_t)kb0 * (D / 32));
 }
 
 template <int D, int KT>
 __device__ __forceinline__ void stage_store(uint8_t* stage, const StagePlan<D, KT>& pl,
-                                            const uint4 (&reg)[Stage<D, KT>::PER_WAVE]) {
+                                            const u32x4 (&reg)[Stage<D, KT>::PER_WAVE]) {
 #pragma unroll
   for (int j = 0; j < Stage<D, KT>::PER_WAVE; j++)
-    *reinterpret_cast<uint4*>(stage + pl.dst[j]) = reg[j];
+    *reinterpret_cast<u32x4*>(stage + pl.dst[j]) = reg[j];
 }
 
 // V_hat operands read from an LDS stage.
@@ -414,11 +414,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     }
   }
 
+  // Copy pipeline: the bytes of tile t+1 are loaded into registers right after
+  // the barrier that ends tile t-1, written to the free LDS stage after tile
+  // t's compute, and published by the barrier that ends tile t.  Each load is
+  // thus in flight across a whole tile of compute (and, crossing the loop's
+  // back edge, cannot be sunk to its use).  Loads past the last tile re-read
+  // the last tile (in bounds; never read back).
   StagePlan<D, KT> plan;
   make_plan<D, KT>(kv, plan);
-  uint4 stage_reg[S::PER_WAVE];
+  const int last_kb0 = (tiles - 1) * KT;
+  u32x4 stage_reg[S::PER_WAVE];
   stage_load<D, KT>(plan, 0, stage_reg);
   stage_store<D, KT>(smem, plan, stage_reg);
+  stage_load<D, KT>(plan, tiles > 1 ? KT : 0, stage_reg);
   __syncthreads();
 
   v16f accO[CT];
@@ -427,10 +435,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   float m = kNegInf, l = 0.0f;
   for (int t = 0; t < tiles; t++) {
     const int kb0 = t * KT;
-    // copy the next tile into the other stage while this one is computed; the
-    // last iteration re-copies its own tile (in bounds; that stage is not read again)
-    const int next_kb0 = (t + 1 < tiles) ? kb0 + KT : kb0;
-    stage_load<D, KT>(plan, next_kb0, stage_reg);
     const uint8_t* st = smem + (t & 1) * S::BYTES;
     if (wave_active && kb0 <= wave_last_key) {
       v16f sacc[NB];
@@ -450,6 +454,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     }
     stage_store<D, KT>(smem + ((t + 1) & 1) * S::BYTES, plan, stage_reg);
     __syncthreads();
+    const int kb2 = kb0 + 2 * KT;
+    stage_load<D, KT>(plan, kb2 <= last_kb0 ? kb2 : last_kb0, stage_reg);
   }
 
   if (wave_active && qrow < p.N_q) store_out<D>(p.out + (bh * p.N_q + qrow) * D, accO, l);

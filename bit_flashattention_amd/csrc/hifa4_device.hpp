@@ -18,6 +18,7 @@ namespace hifa4 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes in 4 VGPRs
 
 // One 32x32x64 E2M1 x E2M1 MFMA: acc += (A * 2^(sa-127)) (B * 2^(sb-127)),
 // with the scale bytes taken from byte OPA of sa and byte OPB of sb.
