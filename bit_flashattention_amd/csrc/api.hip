@@ -139,6 +139,8 @@ hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void
   if (B < 0 || Hq <= 0 || Hkv <= 0 || N_q < 0 || N_kv < 0 || Hq % Hkv != 0)
     return fail(HIFA4_EINVAL, "quantize: need B, N >= 0, Hq, Hkv > 0, Hq %% Hkv == 0");
   if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "quantize: d must be a positive multiple of 32");
+  if (v_f16 && d != 64 && d != 128 && d != 256)
+    return fail(HIFA4_EUNSUPPORTED, "quantize: V needs d in {64, 128, 256}");
   if (smooth && ((q_f16 && !s) || (k_f16 && !inv_s)))
     return fail(HIFA4_EINVAL, "quantize: smooth = 1 needs s (for Q) and inv_s (for K)");
   if ((q_f16 && (!q_codes || !q_scales)) || (k_f16 && (!k_codes || !k_scales)) ||

@@ -606,19 +606,37 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
   const int t0 = chunk * p.tiles_per_split;
   const int t1 = p.n_tiles < t0 + p.tiles_per_split ? p.n_tiles : t0 + p.tiles_per_split;
   if (t0 < t1) {
-    RegOps<D, KT> op;
-    reg_load_k<D, KT>(kv, t0 * KT, op);
-    reg_load_v<D, KT>(kv, t0 * KT, op);
-    for (int t = t0; t < t1; t++) {
-      const int kb0 = t * KT;
-      const bool more = t + 1 < t1;
-      v16f sacc[NB];
+    // Streaming from HBM: three operand sets in a ring keep two tiles in flight
+    // while one is computed.  Loads past the chunk re-read its last tile (in
+    // bounds, never used); the scheduling barriers keep each load where it is
+    // issued instead of letting it sink to its use.
+    RegOps<D, KT> o0, o1, o2;
+    auto kbc = [&](int t) { return (t < t1 ? t : t1 - 1) * KT; };
+    auto load = [&](RegOps<D, KT>& op, int t) {
+      reg_load_k<D, KT>(kv, kbc(t), op);
+      reg_load_v<D, KT>(kv, kbc(t), op);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto tile = [&](RegOps<D, KT>& op, int t) {
+      if (t < t1) {
+        const int kb0 = t * KT;
+        v16f sacc[NB];
 #pragma unroll
-      for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(op.ka[bb], op.ksw[bb], qb, qsc);
-      if (more) reg_load_k<D, KT>(kv, kb0 + KT, op);
-      const bool need_mask = (kb0 + KT - 1) > wave_lim;
-      softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, op, accO, m, l, phc, phs);
-      if (more) reg_load_v<D, KT>(kv, kb0 + KT, op);
+        for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(op.ka[bb], op.ksw[bb], qb, qsc);
+        const bool need_mask = (kb0 + KT - 1) > wave_lim;
+        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, op, accO, m, l, phc, phs);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load(o0, t0);
+    load(o1, t0 + 1);
+    for (int t = t0; t < t1; t += 3) {
+      load(o2, t + 2);
+      tile(o0, t);
+      load(o0, t + 3);
+      tile(o1, t + 1);
+      load(o1, t + 4);
+      tile(o2, t + 2);
     }
   }
 
@@ -645,30 +663,36 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
 // ---------------------------------------------------------------------------
 // Merge of split partials, in chunk order: M = max m_k, w_k = 2^(m_k - M),
 // L = sum w_k l_k, A = sum w_k O_k (fp32, sequential), out = fp16(A / fp16(L)).
-// One thread per (row, channel).
+// One thread per (row, 4 channels): 16-byte partial loads, 8-byte stores.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws_o,
                                                          const float* __restrict__ ws_ml,
                                                          int64_t rows, int d, int C,
                                                          uint16_t* __restrict__ out) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= rows * d) return;
-  const int64_t row = t / d;
-  const int ch = (int)(t % d);
+  const int q = d / 4;
+  if (t >= rows * q) return;
+  const int64_t row = t / q;
+  const int c4 = (int)(t % q);
   const float* ml = ws_ml + row * C * 2;
   float M = kNegInf;
   for (int k = 0; k < C; k++) M = fmaxf(M, ml[2 * k]);
-  float L = 0.0f, A = 0.0f;
+  float L = 0.0f;
+  float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int k = 0; k < C; k++) {
     const float mk = ml[2 * k];
     const float w = (mk == kNegInf) ? 0.0f : exp2_hw(mk - M);
     const float wl = w * ml[2 * k + 1];
     L = L + wl;
-    const float wo = w * ws_o[(row * C + k) * d + ch];
-    A = A + wo;
+    const float4 o = *reinterpret_cast<const float4*>(ws_o + (row * C + k) * d + 4 * c4);
+    const float wo[4] = {w * o.x, w * o.y, w * o.z, w * o.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) A[i] = A[i] + wo[i];
   }
   const float lf = round_f16(L);
-  out[t] = float_to_half_bits(A / lf);
+  const uint32_t lo = (uint32_t)float_to_half_bits(A[0] / lf) | ((uint32_t)float_to_half_bits(A[1] / lf) << 16);
+  const uint32_t hi = (uint32_t)float_to_half_bits(A[2] / lf) | ((uint32_t)float_to_half_bits(A[3] / lf) << 16);
+  *reinterpret_cast<uint2*>(out + row * d + 4 * c4) = make_uint2(lo, hi);
 }
 
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
@@ -689,7 +713,7 @@ hipError_t launch_split_t(const KParams& kp, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || kp.num_splits == 1) return e;
   const int64_t rows = kp.B * kp.Hq * kp.N_q;
-  const int64_t n = rows * D;
+  const int64_t n = rows * (D / 4);
   attn_merge_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
       kp.ws_o, kp.ws_ml, rows, D, kp.num_splits, kp.out);
   return hipGetLastError();

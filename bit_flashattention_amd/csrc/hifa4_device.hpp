@@ -29,6 +29,12 @@ __device__ __forceinline__ v16f mfma_fp4(const uint4& a, int sa, const uint4& b,
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, OPA, sa, OPB, sb);
 }
 
+__device__ __forceinline__ v16f mfma_fp4_v(const u32x4& a, int sa, const u32x4& b, int sb, v16f acc) {
+  v8i A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  v8i B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ v16f zero16() {
   v16f z;
 #pragma unroll

@@ -36,100 +36,107 @@ __global__ void calib_absmax_kernel(const uint16_t* __restrict__ q, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Q / K along channels.  One thread per 8 channels of one token row; the four
-// threads of an aligned quad form one 32-channel block.  Rows >= N of the
-// padded layout are written as zero codes with scale byte 0.
+// Q / K along channels.  One thread per 32-channel block of one token row
+// (64 bytes in, 16 code bytes + 1 scale byte out); consecutive threads cover
+// consecutive blocks, so a wavefront reads 4 KB and writes 1 KB contiguously.
+// Rows >= N of the padded layout are written as zero codes with scale byte 0.
 //   x = fp32(x_f16 * mult[g][j])   (mult = s for Q, inv_s for K; NULL: none)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mult, int64_t H, int64_t G,
-    int64_t N, int64_t Npad, int64_t d, int64_t total_threads, uint32_t* __restrict__ codes,
+    int64_t N, int64_t Npad, int64_t d, int64_t total_threads, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= total_threads) return;  // total_threads is a multiple of 4: quads stay whole
-  const int64_t per_row = d / 8;
-  const int64_t row = t / per_row, part = t % per_row;
+  if (t >= total_threads) return;
+  const int64_t per_row = d / 32;
+  const int64_t row = t / per_row, blk = t % per_row;
   const int64_t bh = row / Npad, n = row % Npad;
-  float v[8];
+  u32x4 out = {0u, 0u, 0u, 0u};
+  uint8_t sc = 0;
   if (n < N) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + ((bh * N + n) * d + part * 8));
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + ((bh * N + n) * d + blk * 32));
+    float v[32];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      v[2 * i] = half_to_float((uint16_t)(w[i] & 0xFFFFu));
-      v[2 * i + 1] = half_to_float((uint16_t)(w[i] >> 16));
+    for (int u = 0; u < 4; u++) {
+      const u32x4 raw = src[u];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[8 * u + 2 * i] = half_to_float((uint16_t)(raw[i] & 0xFFFFu));
+        v[8 * u + 2 * i + 1] = half_to_float((uint16_t)(raw[i] >> 16));
+      }
     }
     if (mult) {
-      const int64_t g = (bh % H) / G;
-      const float4* mp = reinterpret_cast<const float4*>(mult + g * d + part * 8);
-      const float4 m0 = mp[0], m1 = mp[1];
-      v[0] = v[0] * m0.x; v[1] = v[1] * m0.y; v[2] = v[2] * m0.z; v[3] = v[3] * m0.w;
-      v[4] = v[4] * m1.x; v[5] = v[5] * m1.y; v[6] = v[6] * m1.z; v[7] = v[7] * m1.w;
+      const float4* mp = reinterpret_cast<const float4*>(mult + ((bh % H) / G) * d + blk * 32);
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const float4 mm = mp[u];
+        v[4 * u] = v[4 * u] * mm.x;
+        v[4 * u + 1] = v[4 * u + 1] * mm.y;
+        v[4 * u + 2] = v[4 * u + 2] * mm.z;
+        v[4 * u + 3] = v[4 * u + 3] * mm.w;
+      }
     }
-  } else {
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const int e = mx_exponent(amax);
+    const float scale = pow2f(e);
+#pragma unroll
+    for (int w = 0; w < 4; w++) out[w] = pack8_fp4(&v[8 * w], scale);
+    sc = (uint8_t)(e + 127);
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
-  amax = quad_max(amax);
-  const int e = mx_exponent(amax);
-  const uint32_t w = pack8_fp4(v, pow2f(e));
-  codes[row * (d / 8) + part] = (n < N) ? w : 0u;
-  if ((part & 3) == 0) scales[row * (d / 32) + part / 4] = (n < N) ? (uint8_t)(e + 127) : (uint8_t)0;
+  *reinterpret_cast<u32x4*>(codes + row * (d / 2) + blk * 16) = out;
+  scales[row * (d / 32) + blk] = sc;
 }
 
 // ---------------------------------------------------------------------------
 // V along tokens, written in the tiled token layout: for each 64-token tile,
 // each channel's 32 code bytes (tokens 64t..64t+63, two 32-token blocks) are
 // contiguous, channels one after another: codes [B][H][Npad/64][d][32],
-// scales [B][H][Npad/64][d][2].  One thread per (4 channels, 32-token block):
-// it reads the block's 32 token rows as 8-byte pieces (neighbouring threads
-// read neighbouring channels of the same token, so loads coalesce) and writes
-// one 16-byte code block + one scale byte per channel.  Tokens >= N count as 0.
+// scales [B][H][Npad/64][d][2].  One workgroup per 64-token tile: it reads the
+// tile's 64 token rows (64 x d binary16, coalesced 16-byte loads) into LDS,
+// then each thread quantizes one (channel, 32-token block) from a column of
+// the LDS tile and writes its 16 code bytes; the workgroup's writes are one
+// contiguous range.  Tokens >= N count as 0.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, int64_t N,
-                                                      int64_t Npad, int64_t d,
-                                                      int64_t total_threads,
-                                                      uint8_t* __restrict__ codes,
+                                                      int64_t Npad, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= total_threads) return;
-  const int64_t groups = d / 4, nblk = Npad / 32;
-  const int64_t cg = t % groups;
-  const int64_t beta = (t / groups) % nblk;
-  const int64_t bh = t / (groups * nblk);
-  float x[4][32];
+  constexpr int ROW = D + 8;  // padded LDS row (binary16 elements): spreads column reads over banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile_lds[64 * ROW];
+  const int64_t tiles = Npad / 64;
+  const int64_t tile = blockIdx.x;  // (b*H + h) * tiles + tile index
+  const int64_t bh = tile / tiles, t64 = tile % tiles;
+  const int tid = threadIdx.x;
+  // load 64 rows x D channels: D/8 16-byte pieces per row
+  constexpr int PIECES = 64 * D / 8;
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
-    const int64_t n = beta * 32 + i;
-    if (n < N) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(v + ((bh * N + n) * d + cg * 4));
-      x[0][i] = half_to_float((uint16_t)(raw.x & 0xFFFFu));
-      x[1][i] = half_to_float((uint16_t)(raw.x >> 16));
-      x[2][i] = half_to_float((uint16_t)(raw.y & 0xFFFFu));
-      x[3][i] = half_to_float((uint16_t)(raw.y >> 16));
-    } else {
-      x[0][i] = x[1][i] = x[2][i] = x[3][i] = 0.0f;
-    }
+  for (int i = tid; i < PIECES; i += 256) {
+    const int r = i / (D / 8), c8 = i % (D / 8);
+    const int64_t n = t64 * 64 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (n < N) val = *reinterpret_cast<const u32x4*>(v + (bh * N + n) * D + c8 * 8);
+    *reinterpret_cast<u32x4*>(&tile_lds[r * ROW + c8 * 8]) = val;
   }
-  const int64_t tile = bh * (Npad / 64) + beta / 2;
+  __syncthreads();
+  // (block, channel) pairs: 2 * D of them; a wavefront reads 64 consecutive
+  // channels of one LDS row per step (no bank conflicts)
+  for (int i = tid; i < 2 * D; i += 256) {
+    const int blk = i / D, ch = i % D;
+    float x[32];
 #pragma unroll
-  for (int c = 0; c < 4; c++) {
+    for (int k = 0; k < 32; k++) x[k] = half_to_float(tile_lds[(blk * 32 + k) * ROW + ch]);
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(x[c][i]));
+    for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(x[k]));
     const int e = mx_exponent(amax);
     const float sc = pow2f(e);
-    uint4 out;
-    out.x = pack8_fp4(&x[c][0], sc);
-    out.y = pack8_fp4(&x[c][8], sc);
-    out.z = pack8_fp4(&x[c][16], sc);
-    out.w = pack8_fp4(&x[c][24], sc);
-    const int64_t ch = tile * d + cg * 4 + c;
-    *reinterpret_cast<uint4*>(codes + ch * 32 + (beta % 2) * 16) = out;
-    scales[ch * 2 + (beta % 2)] = (uint8_t)(e + 127);
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; w++) out[w] = pack8_fp4(&x[8 * w], sc);
+    *reinterpret_cast<u32x4*>(codes + (tile * D + ch) * 32 + blk * 16) = out;
+    scales[(tile * D + ch) * 2 + blk] = (uint8_t)(e + 127);
   }
 }
 
@@ -151,24 +158,28 @@ hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_
                              int64_t N, int64_t d, uint8_t* codes, uint8_t* scales,
                              hipStream_t stream) {
   const int64_t Npad = pad_tokens(N);
-  const int64_t total = B * H * Npad * (d / 8);
+  const int64_t total = B * H * Npad * (d / 32);
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   quant_rows_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
-      (const uint16_t*)x, mult, H, H / Hkv, N, Npad, d, total, (uint32_t*)codes, scales);
+      (const uint16_t*)x, mult, H, H / Hkv, N, Npad, d, total, codes, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   const int64_t Npad = pad_tokens(N);
-  const int64_t total = B * H * (Npad / 32) * (d / 4);
-  if (total == 0) return hipSuccess;
-  const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
-  quant_v_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
-      (const uint16_t*)v, N, Npad, d, total, codes, scales);
+  const int64_t tiles = B * H * (Npad / 64);
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)tiles), block(256);
+  const uint16_t* vv = (const uint16_t*)v;
+  switch (d) {
+    case 64: quant_v_kernel<64><<<grid, block, 0, stream>>>(vv, N, Npad, codes, scales); break;
+    case 128: quant_v_kernel<128><<<grid, block, 0, stream>>>(vv, N, Npad, codes, scales); break;
+    case 256: quant_v_kernel<256><<<grid, block, 0, stream>>>(vv, N, Npad, codes, scales); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
