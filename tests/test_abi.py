@@ -78,7 +78,8 @@ def _args(hf, **kw):
     (dict(N_q=300, N_kv=256, causal=1), "EINVAL"),
     (dict(d=100), "EINVAL"),
     (dict(d=96), "EUNSUPPORTED"),
-    (dict(args=dict(kv_tile=128)), "EUNSUPPORTED"),
+    (dict(args=dict(kv_tile=128), d=256), "EUNSUPPORTED"),
+    (dict(args=dict(kv_tile=96)), "EUNSUPPORTED"),
     (dict(args=dict(num_splits=0)), "EINVAL"),
     (dict(args=dict(q_f16=0x2000)), "EINVAL"),          # both Q forms given
     (dict(args=dict(k_codes=None)), "EINVAL"),
