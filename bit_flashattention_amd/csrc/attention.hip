@@ -10,13 +10,13 @@
 //    FP4 MFMA 32x32x64: A = 32 keys (16 bytes of one K_hat row per lane),
 //    B = the wave's 32 query rows (loop-invariant registers).  The
 //    accumulator gives each lane one query column and 16 keys.
-//  * One v_permlane32_swap per register pair turns two 32-key S^T blocks into
-//    "lane = (query, 32-key block)": every lane then holds exactly the 32
-//    keys that share one P_hat scale.  Block max, exp, block exponent and the
-//    E2M1 conversion run in-lane; the row max needs one more swap.
-//  * P_hat is then already the B operand of O^T = V_hat^T P_hat^T (A = 32
-//    channels x 64 keys of V_hat), so the output accumulator is "lane =
-//    query" too: alpha, m and l never leave their lane.
+//  * Each lane holds 16 keys of every 32-key block for its query; max, exp
+//    and the E2M1 conversion run in place on those registers.  The two lanes
+//    of a query exchange only each block's partial max and the packed codes
+//    (v_permlane32_swap), after which every lane holds one full 32-key block:
+//    the B operand of O^T = V_hat^T P_hat^T (A = 32 channels x 64 keys of
+//    V_hat, whose tokens are stored in the same in-block order).  The output
+//    accumulator is "lane = query" too: alpha, m and l never leave their lane.
 //  * P-Reordering: one more MFMA with A = all-ones E2M1 codes yields
 //    rowsum(P_hat) -- the normalizer is a row of the same PV product
 //    ([V_hat | 1]) instead of a VALU reduction.
@@ -72,89 +72,120 @@ __device__ __forceinline__ v16f score_block(const uint4 (&ka)[D / 64], const uin
   return acc;
 }
 
+// Block exponent of P_hat from the block's largest valid score (bmax = -inf:
+// no valid key, -127): e = clamp(floor(fma(bmax, c, -m)) - 2, -127, 127).
+__device__ __forceinline__ int phat_exponent(float bmax, float c, float m_use) {
+  const float ef = __builtin_amdgcn_fmed3f(floorf(__builtin_fmaf(bmax, c, -m_use)) - 2.0f, -127.0f, 127.0f);
+  return (int)ef;
+}
+
+// Four E2M1 code bytes (8 values, value i in nibble i) of S^T registers
+// r0..r0+7 of one block, RNE(x / sc).
+__device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
+  uint32_t w = cvt_fp4x2<0>(0u, x[r0], x[r0 + 1], sc);
+  w = cvt_fp4x2<1>(w, x[r0 + 2], x[r0 + 3], sc);
+  w = cvt_fp4x2<2>(w, x[r0 + 4], x[r0 + 5], sc);
+  return cvt_fp4x2<3>(w, x[r0 + 6], x[r0 + 7], sc);
+}
+
 // The online-softmax step of one tile of KT keys given its S^T blocks:
 // running max, P, P_hat, normalizer, O rescale and O^T += V_hat^T P_hat^T.
 // vops.a(u, ct) / vops.sc(ct) supply the V_hat operands (byte 2u of the scale
 // word is unit u's block).  lim: last valid key of this lane's query column.
+//
+// Lane (query q, half hf) holds, of every 32-key block, the 16 keys with bit 2
+// of the key index equal to hf (S^T accumulator register r: key 8(r/4) + 4hf
+// + r%4).  All per-element work runs on these registers in place; the lanes of
+// a pair (q, 0) / (q, 1) exchange only each block's partial max (one
+// permlane32 swap per value) and the packed codes (one swap per two dwords),
+// after which lane (q, hf) holds the full 32-code block 2u + hf of unit u --
+// the B operand of the PV product -- with its keys in the operand order
+// operand_key (the V_hat tiled layout stores tokens in the same order).
 template <int D, int KT, bool REORDER, bool DUMP, class VOps>
-__device__ __forceinline__ void softmax_pv(v16f (&sacc)[KT / 32], int kb0, bool need_mask, int lim,
+__device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
                                            float c, const VOps& vops, v16f (&accO)[D / 32],
                                            float& m, float& l, uint8_t* phat_codes_row,
                                            uint8_t* phat_scales_row) {
-  constexpr int CT = D / 32, NU = KT / 64;
+  constexpr int CT = D / 32, NB = KT / 32, NU = KT / 64;
   const int hf = (threadIdx.x >> 5) & 1;
 
-  // lane = (query, 32-key block 2u + hf): X[u][r] is key 8(r/4) + r%4 of the
-  // block, Y[u][r] the key 4 further.
-  float X[NU][16], Y[NU][16];
-#pragma unroll
-  for (int u = 0; u < NU; u++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sacc[2 * u][r]),
-                                                 __float_as_uint(sacc[2 * u + 1][r]), false, false);
-      X[u][r] = __uint_as_float(sw[0]);
-      Y[u][r] = __uint_as_float(sw[1]);
-    }
   if (need_mask) {
+    // key offset o within the tile is valid when o <= room; the select is done
+    // with a sign mask and a bitfield insert so that it needs no scalar masks
+    const int room = lim - kb0 - 4 * hf;
 #pragma unroll
-    for (int u = 0; u < NU; u++) {
-      const int base = kb0 + 64 * u + 32 * hf;
+    for (int bb = 0; bb < NB; bb++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int kx = base + 8 * (r / 4) + (r % 4);
-        if (kx > lim) X[u][r] = kNegInf;
-        if (kx + 4 > lim) Y[u][r] = kNegInf;
+        const int o = 32 * bb + 8 * (r / 4) + (r % 4);
+        const uint32_t drop = (uint32_t)((room - o) >> 31);  // all ones when o > room
+        s[bb][r] = __uint_as_float((drop & 0xFF800000u) | (~drop & __float_as_uint(s[bb][r])));
       }
-    }
   }
 
-  // running max (log2 domain, FP16 state)
-  float bm[NU];
+  // block maxima: this lane's 16 keys, then the partner lane's 16
+  float pm[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; bb++) {
+    float x = fmaxf(s[bb][0], s[bb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r++) x = fmaxf(x, s[bb][r]);
+    pm[bb] = x;
+  }
+  // mine[u]: max of block 2u + hf (the block this lane holds after the code
+  // exchange); oth[u]: max of block 2u + 1 - hf
+  float mine[NU], oth[NU];
   float rmax = kNegInf;
 #pragma unroll
   for (int u = 0; u < NU; u++) {
-    float x = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; r++) x = fmaxf(x, fmaxf(X[u][r], Y[u][r]));
-    bm[u] = x;
-    rmax = fmaxf(rmax, x);
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[2 * u]), __float_as_uint(pm[2 * u + 1]), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[2 * u + 1]), __float_as_uint(pm[2 * u]), false, false);
+    mine[u] = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    oth[u] = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    rmax = fmaxf(rmax, fmaxf(mine[u], oth[u]));
   }
-  const float smax = fmaxf(rmax, other_half(rmax));
-  const float mt = c * smax;
+
+  // running max (log2 domain, FP16 state)
+  const float mt = c * rmax;
   const float m_new = round_f16(fmaxf(m, mt));
   const float m_use = (m_new == kNegInf) ? 0.0f : m_new;  // column with no valid key yet
   const float alpha = exp2_hw(m - m_use);
 
-  // P = 2^(S c - m); each block's exponent from its largest t
-#pragma unroll
-  for (int u = 0; u < NU; u++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      X[u][r] = exp2_hw(__builtin_fmaf(X[u][r], c, -m_use));
-      Y[u][r] = exp2_hw(__builtin_fmaf(Y[u][r], c, -m_use));
-    }
-  uint4 ph[NU];
+  // per-block exponents; sc[bb]: the scale of block bb for this lane's elements
+  float sc[NB];
   int psc[NU];
 #pragma unroll
   for (int u = 0; u < NU; u++) {
-    const float tmax = __builtin_fmaf(bm[u], c, -m_use);
-    const float ef = fminf(fmaxf(floorf(tmax) - 2.0f, -127.0f), 127.0f);
-    const int e = (int)ef;
-    const float sc = pow2f(e);
-    uint32_t pw[4];
+    const int em = phat_exponent(mine[u], c, m_use);
+    const int eo = phat_exponent(oth[u], c, m_use);
+    const float sm = pow2f(em), so = pow2f(eo);
+    sc[2 * u] = hf ? so : sm;
+    sc[2 * u + 1] = hf ? sm : so;
+    psc[u] = em + 127;
+  }
+
+  // P = 2^(S c - m)
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
-      uint32_t x = cvt_fp4x2<0>(0u, X[u][4 * w], X[u][4 * w + 1], sc);
-      x = cvt_fp4x2<1>(x, X[u][4 * w + 2], X[u][4 * w + 3], sc);
-      x = cvt_fp4x2<2>(x, Y[u][4 * w], Y[u][4 * w + 1], sc);
-      pw[w] = cvt_fp4x2<3>(x, Y[u][4 * w + 2], Y[u][4 * w + 3], sc);
-    }
-    ph[u] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-    psc[u] = e + 127;
+  for (int bb = 0; bb < NB; bb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) s[bb][r] = exp2_hw(__builtin_fmaf(s[bb][r], c, -m_use));
+
+  // P_hat codes: this lane's 16 keys of each block as two dwords, then one
+  // swap per dword pair hands each lane the partner's half of its block
+  uint4 ph[NU];
+#pragma unroll
+  for (int u = 0; u < NU; u++) {
+    const uint32_t a0 = cvt8(s[2 * u], 0, sc[2 * u]), a1 = cvt8(s[2 * u], 8, sc[2 * u]);
+    const uint32_t b0 = cvt8(s[2 * u + 1], 0, sc[2 * u + 1]), b1 = cvt8(s[2 * u + 1], 8, sc[2 * u + 1]);
+    auto w0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    auto w1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    ph[u] = make_uint4(w0[0], w1[0], w0[1], w1[1]);
     if constexpr (DUMP) {
       if (phat_codes_row) {
-        *reinterpret_cast<uint4*>(phat_codes_row + kb0 / 2 + 32 * u + 16 * hf) = ph[u];
+        // back to ascending key order (operand_key inverted on 16-bit groups)
+        const uint4 k = make_uint4((ph[u].x & 0xFFFFu) | (ph[u].z << 16), (ph[u].x >> 16) | (ph[u].z & 0xFFFF0000u),
+                                   (ph[u].y & 0xFFFFu) | (ph[u].w << 16), (ph[u].y >> 16) | (ph[u].w & 0xFFFF0000u));
+        *reinterpret_cast<uint4*>(phat_codes_row + kb0 / 2 + 32 * u + 16 * hf) = k;
         phat_scales_row[kb0 / 32 + 2 * u + hf] = (uint8_t)psc[u];
       }
     }
@@ -181,12 +212,9 @@ __device__ __forceinline__ void softmax_pv(v16f (&sacc)[KT / 32], int kb0, bool 
   } else {
     rs = 0.0f;
 #pragma unroll
-    for (int u = 0; u < NU; u++)
+    for (int bb = 0; bb < NB; bb++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        rs = rs + X[u][r];
-        rs = rs + Y[u][r];
-      }
+      for (int r = 0; r < 16; r++) rs = rs + s[bb][r];
     rs = rs + other_half(rs);
   }
   const float al = alpha * l;

@@ -20,6 +20,15 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes in 4 VGPRs
 
+// Key order inside a 32-key operand block of P_hat (B operand of the PV
+// product) and of V_hat (its A operand): nibble k of the block's 16 bytes holds
+// key operand_key(k) of the block.  In binary, k = (k4 k3 k2 k1 k0) holds key
+// (k3 k2 k4 k1 k0): the S^T accumulator gives lane half hf the keys whose bit 2
+// is hf, and packing those first needs no per-element lane exchange.
+__host__ __device__ constexpr int operand_key(int k) {
+  return (((k >> 3) & 1) << 4) | (((k >> 2) & 1) << 3) | ((k >> 4) << 2) | (k & 3);
+}
+
 // One 32x32x64 E2M1 x E2M1 MFMA: acc += (A * 2^(sa-127)) (B * 2^(sb-127)),
 // with the scale bytes taken from byte OPA of sa and byte OPB of sb.
 template <int OPA, int OPB>

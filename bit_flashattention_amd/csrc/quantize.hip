@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // V along tokens, written in the tiled token layout: for each 64-token tile,
 // each channel's 32 code bytes (tokens 64t..64t+63, two 32-token blocks) are
 // contiguous, channels one after another: codes [B][H][Npad/64][d][32],
-// scales [B][H][Npad/64][d][2].  One workgroup per 64-token tile: it reads the
+// scales [B][H][Npad/64][d][2].  Inside a 32-token block, nibble k holds
+// token operand_key(k) (the PV product's operand order).  One workgroup per 64-token tile: it reads the
 // tile's 64 token rows (64 x d binary16, coalesced 16-byte loads) into LDS,
 // then each thread quantizes one (channel, 32-token block) from a column of
 // the LDS tile and writes its 16 code bytes; the workgroup's writes are one
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     const int blk = i / D, ch = i % D;
     float x[32];
 #pragma unroll
-    for (int k = 0; k < 32; k++) x[k] = half_to_float(tile_lds[(blk * 32 + k) * ROW + ch]);
+    for (int k = 0; k < 32; k++) x[k] = half_to_float(tile_lds[(blk * 32 + operand_key(k)) * ROW + ch]);
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(x[k]));

@@ -32,7 +32,10 @@
  *                          [B][H][Npad/64][d][2]: blocks of 32 consecutive
  *                          tokens of one channel; per 64-token tile, each
  *                          channel's two blocks (32 code bytes, 2 scale bytes)
- *                          are contiguous, channel after channel.
+ *                          are contiguous, channel after channel.  Inside a
+ *                          block the 32 tokens are stored in the MFMA operand
+ *                          order: nibble k (k = k4..k0 in binary) holds token
+ *                          (k3 k2 k4 k1 k0) of the block.
  * - Errors: argument checks run first, on the host, and touch no device:
  *   HIFA4_EINVAL (bad sizes, NULL where a buffer is required, misaligned
  *   pointers), HIFA4_EUNSUPPORTED (valid but not built: d not 64/128/256,

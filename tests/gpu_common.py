@@ -57,13 +57,26 @@ def mx4_to_dev(pair):
     return hf.MX4(to_dev(pair[0]), to_dev(pair[1]))
 
 
+def operand_key(k: int) -> int:
+    """Token of a 32-token block stored at nibble k in the library's V_hat layout:
+    the bits (k4 k3 k2 k1 k0) of k name token (k3 k2 k4 k1 k0)."""
+    return (((k >> 3) & 1) << 4) | (((k >> 2) & 1) << 3) | ((k >> 4) << 2) | (k & 3)
+
+
+OPERAND_ORDER = np.array([operand_key(k) for k in range(32)])
+
+
 def tile_v(pair):
     """Canonical V_hat ([B][H][d][Npad/2] codes, [B][H][d][Npad/32] scales) -> the
-    library's tiled token layout ([B][H][Npad/64][d][32], [B][H][Npad/64][d][2]).
-    A pure re-arrangement of bytes: no value changes."""
+    library's tiled token layout ([B][H][Npad/64][d][32], [B][H][Npad/64][d][2]) with
+    each 32-token block's nibbles in operand order.  A pure re-arrangement of 4-bit
+    codes: no value changes."""
     codes, scales = pair
     B, H, d, nb = codes.shape
     t = nb // 32
+    nib = oracle.unpack_nibbles(codes).reshape(B, H, d, -1, 32)[..., OPERAND_ORDER]
+    nib = nib.reshape(B, H, d, -1, 16, 2).astype(np.uint8)
+    codes = (nib[..., 0] | (nib[..., 1] << 4)).reshape(B, H, d, nb)
     c = np.ascontiguousarray(codes.reshape(B, H, d, t, 32).transpose(0, 1, 3, 2, 4))
     s = np.ascontiguousarray(scales.reshape(B, H, d, t, 2).transpose(0, 1, 3, 2, 4))
     return c, s
