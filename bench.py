@@ -91,8 +91,14 @@ def prepare_prefill(w, hf, torch):
     return dict(q=q, k=k, v=v, s=s, inv=inv, bufs=bufs, out=out)
 
 
-def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=64):
+def default_kv_tile(d: int) -> int:
+    """Keys per tile: 128 where the kernels support it (d <= 128), else 64."""
+    return 128 if d <= 128 else 64
+
+
+def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None):
     """Time `steps` full steps (quantize + attention).  Returns (ms/step, attention kernel ms)."""
+    kv_tile = kv_tile or default_kv_tile(w.d)
     st = prepare_prefill(w, hf, torch)
     q4, k4, v4 = st["bufs"]
 
@@ -179,12 +185,16 @@ def parity_sample(w, hf, st, rows, reorder=True):
     rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
     rv = oracle.quantize_v(w.v)
     ref = oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=int(reorder),
-                      q4=rq, k4=rk, v4=rv, rows=rows)
+                      kv_tile=default_kv_tile(w.d), q4=rq, k4=rk, v4=rv, rows=rows)
     got = st["out"].reshape(-1, w.d)[rows].cpu().numpy().astype(np.float64)
     exp = ref["out"].view(np.float16).astype(np.float64)
     rowmax = np.abs(exp).max(axis=1, keepdims=True)
     e = np.abs(got - exp) / rowmax
-    return float(e.max()), float(e.mean())
+    # error of the 4-bit path against fp64 softmax attention on the binary16 inputs
+    exact = oracle.attn_exact(w.q, w.k, w.v, w.causal, rows=rows)
+    ex_max = np.abs(exact).max(axis=1, keepdims=True)
+    ee = np.abs(got - exact) / ex_max
+    return float(e.max()), float(e.mean()), float(ee.max()), float(ee.mean())
 
 
 def cpu_baseline(w, target_s=12.0, seed=777):
@@ -203,8 +213,8 @@ def cpu_baseline(w, target_s=12.0, seed=777):
 
     def timed(rows):
         t0 = time.perf_counter()
-        oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=1, q4=rq,
-                    k4=rk, v4=rv, rows=rows, threads=threads)
+        oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=1,
+                    kv_tile=default_kv_tile(w.d), q4=rq, k4=rk, v4=rv, rows=rows, threads=threads)
         return time.perf_counter() - t0
 
     probe = sample_rows(w, 1024, seed=seed + 1)
@@ -271,9 +281,11 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic (seeded SplitMix64/Box-Muller, RoPE, outlier channels; no model weights)",
         "config": {"workload": "qwen3_8b_prefill", "B": 1, "Hq": 32, "Hkv": 8, "N": 4096, "d": 128,
-                   "causal": True, "smooth_alpha": 0.5, "reorder": True, "kv_tile": 64,
+                   "causal": True, "smooth_alpha": 0.5, "reorder": True,
+                   "kv_tile": default_kv_tile(w.d),
                    "step": "quantize_qkv + attn_fwd"},
-        "roofline": {"bound": "mfma", "kernel": "attn_prefill_kernel<128,causal,reorder>",
+        "roofline": {"bound": "mfma",
+                     "kernel": f"attn_prefill_kernel<{w.d},{default_kv_tile(w.d)},causal,reorder>",
                      "achieved": round(attn_tflops, 3), "peak": FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 5),
                      "traffic": traffic, "kernel_ms": round(attn_ms, 5)},
@@ -281,9 +293,11 @@ def main():
     extra = {}
     if not a.quick:
         rows = sample_rows(w, 256)
-        emax, emean = parity_sample(w, hf, st, rows, reorder=True)
-        extra["parity_sample"] = {"rows": len(rows), "err_max": emax, "err_mean": emean}
-        log(f"[bench] parity on {len(rows)} sampled rows: max {emax:.2e} mean {emean:.2e}")
+        emax, emean, xmax, xmean = parity_sample(w, hf, st, rows, reorder=True)
+        extra["parity_sample"] = {"rows": len(rows), "err_max": emax, "err_mean": emean,
+                                  "vs_fp64_exact_max": xmax, "vs_fp64_exact_mean": xmean}
+        log(f"[bench] parity on {len(rows)} sampled rows: max {emax:.2e} mean {emean:.2e}; "
+            f"vs fp64 exact attention: max {xmax:.2e} mean {xmean:.2e}")
         del st
         ms0, attn0, st0 = run_prefill(w, hf, torch, a.steps, a.warmup, reorder=False)
         extra["qwen3_8b_reorder_off"] = {"ms_per_step": ms0, "attn_ms": attn0,

@@ -164,14 +164,10 @@ hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void
     if ((st = check_dev_ptr(ptrs[i], names[i]))) return st;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e;
-  if (q_f16 && (e = hifa4::launch_quant_rows(q_f16, smooth ? s : nullptr, B, Hq, Hkv, N_q, d,
-                                              q_codes, q_scales, hs)) != hipSuccess)
-    return hip_fail(e, "quantize Q");
-  if (k_f16 && (e = hifa4::launch_quant_rows(k_f16, smooth ? inv_s : nullptr, B, Hkv, Hkv, N_kv, d,
-                                              k_codes, k_scales, hs)) != hipSuccess)
-    return hip_fail(e, "quantize K");
-  if (v_f16 && (e = hifa4::launch_quant_v(v_f16, B, Hkv, N_kv, d, v_codes, v_scales, hs)) != hipSuccess)
-    return hip_fail(e, "quantize V");
+  if ((e = hifa4::launch_quant_qkv(q_f16, smooth ? s : nullptr, k_f16, smooth ? inv_s : nullptr,
+                                   v_f16, B, Hq, Hkv, N_q, N_kv, d, q_codes, q_scales, k_codes,
+                                   k_scales, v_codes, v_scales, hs)) != hipSuccess)
+    return hip_fail(e, "quantize");
   return ok();
 }
 

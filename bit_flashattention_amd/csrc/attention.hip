@@ -235,18 +235,28 @@ __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool nee
   m = m_new;
 }
 
+// o / l from the hardware reciprocal and one residual correction (Markstein):
+// q = o r, q' = q + (o - q l) r.  With r within 1 ulp of 1/l this is the
+// correctly rounded quotient except in rare boundary cases (then 1 ulp off),
+// far below the binary16 rounding that follows.
+__device__ __forceinline__ float div_by(float o, float l, float r) {
+  const float q = o * r;
+  return __builtin_fmaf(__builtin_fmaf(-q, l, o), r, q);
+}
+
 // Epilogue: out = fp16(O / l) for the lane's query row (channels 32ct + 8(r/4) + 4hf + r%4).
 template <int D>
 __device__ __forceinline__ void store_out(uint16_t* orow, const v16f (&accO)[D / 32], float l) {
   const int hf = (threadIdx.x >> 5) & 1;
+  const float r = __builtin_amdgcn_rcpf(l);
 #pragma unroll
   for (int ct = 0; ct < D / 32; ct++)
 #pragma unroll
     for (int r4 = 0; r4 < 4; r4++) {
-      uint32_t lo = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 0] / l) |
-                    ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 1] / l) << 16);
-      uint32_t hi = (uint32_t)float_to_half_bits(accO[ct][4 * r4 + 2] / l) |
-                    ((uint32_t)float_to_half_bits(accO[ct][4 * r4 + 3] / l) << 16);
+      uint32_t lo = (uint32_t)float_to_half_bits(div_by(accO[ct][4 * r4 + 0], l, r)) |
+                    ((uint32_t)float_to_half_bits(div_by(accO[ct][4 * r4 + 1], l, r)) << 16);
+      uint32_t hi = (uint32_t)float_to_half_bits(div_by(accO[ct][4 * r4 + 2], l, r)) |
+                    ((uint32_t)float_to_half_bits(div_by(accO[ct][4 * r4 + 3], l, r)) << 16);
       *reinterpret_cast<uint2*>(orow + 32 * ct + 8 * r4 + 4 * hf) = make_uint2(lo, hi);
     }
 }

@@ -18,8 +18,11 @@ hipError_t launch_calib_absmax(const void* q, const void* k, int64_t B, int64_t 
 hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_t H, int64_t Hkv,
                              int64_t N, int64_t d, uint8_t* codes, uint8_t* scales,
                              hipStream_t stream);
-hipError_t launch_quant_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
-                          uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const float* inv_s,
+                            const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q,
+                            int64_t N_kv, int64_t d, uint8_t* q_codes, uint8_t* q_scales,
+                            uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                            uint8_t* v_scales, hipStream_t stream);
 
 // Everything one attention launch needs (device pointers + sizes).
 struct AttnLaunch {

@@ -42,12 +42,12 @@ __global__ void calib_absmax_kernel(const uint16_t* __restrict__ q, const uint16
 // Rows >= N of the padded layout are written as zero codes with scale byte 0.
 //   x = fp32(x_f16 * mult[g][j])   (mult = s for Q, inv_s for K; NULL: none)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_rows_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ mult, int64_t H, int64_t G,
-    int64_t N, int64_t Npad, int64_t d, int64_t total_threads, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= total_threads) return;
+template <int D>
+__device__ __forceinline__ void quant_row_block(const uint16_t* __restrict__ x, const float* __restrict__ mult,
+                                                int64_t H, int64_t G, int64_t N, int64_t Npad, int64_t t,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                int64_t d_rt) {
+  const int64_t d = D > 0 ? D : d_rt;
   const int64_t per_row = d / 32;
   const int64_t row = t / per_row, blk = t % per_row;
   const int64_t bh = row / Npad, n = row % Npad;
@@ -89,6 +89,16 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   scales[row * (d / 32) + blk] = sc;
 }
 
+// Any d that is a multiple of 32 (the fused kernel below covers d = 64, 128, 256).
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ mult, int64_t H, int64_t G,
+    int64_t N, int64_t Npad, int64_t d, int64_t total_threads, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total_threads) return;
+  quant_row_block<0>(x, mult, H, G, N, Npad, t, codes, scales, d);
+}
+
 // ---------------------------------------------------------------------------
 // V along tokens, written in the tiled token layout: for each 64-token tile,
 // each channel's 32 code bytes (tokens 64t..64t+63, two 32-token blocks) are
@@ -101,14 +111,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // contiguous range.  Tokens >= N count as 0.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, int64_t N,
-                                                      int64_t Npad, uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, int64_t N, int64_t Npad,
+                                             int64_t tile, uint16_t* tile_lds,
+                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int ROW = D + 8;  // padded LDS row (binary16 elements): spreads column reads over banks
-  __shared__ __attribute__((aligned(16))) uint16_t tile_lds[64 * ROW];
   const int64_t tiles = Npad / 64;
-  const int64_t tile = blockIdx.x;  // (b*H + h) * tiles + tile index
-  const int64_t bh = tile / tiles, t64 = tile % tiles;
+  const int64_t bh = tile / tiles, t64 = tile % tiles;  // tile = (b*H + h) * tiles + tile index
   const int tid = threadIdx.x;
   // load 64 rows x D channels: D/8 16-byte pieces per row
   constexpr int PIECES = 64 * D / 8;
@@ -142,6 +150,41 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Q, K and V of one call in a single launch (d = 64, 128, 256): blocks
+// [0, nq) quantize Q rows, [nq, nq + nk) K rows, the rest one V tile each.
+// One launch instead of three keeps the HBM stream going across the tensors.
+// ---------------------------------------------------------------------------
+struct QuantArgs {
+  const uint16_t* x[2];  // Q, K (NULL: none)
+  const float* mult[2];  // s, inv_s (NULL: no Smooth-QK multiply)
+  int64_t H[2], G[2], N[2], Npad[2], threads[2], blocks[2];
+  uint8_t* codes[2];
+  uint8_t* scales[2];
+  const uint16_t* v;
+  int64_t vN, vNpad;
+  uint8_t* vcodes;
+  uint8_t* vscales;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile_lds[64 * (D + 8)];
+  int64_t b = blockIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    if (b < a.blocks[i]) {
+      const int64_t t = b * 256 + threadIdx.x;
+      if (t < a.threads[i])
+        quant_row_block<D>(a.x[i], a.mult[i], a.H[i], a.G[i], a.N[i], a.Npad[i], t, a.codes[i],
+                           a.scales[i], D);
+      return;
+    }
+    b -= a.blocks[i];
+  }
+  quant_v_tile<D>(a.v, a.vN, a.vNpad, b, tile_lds, a.vcodes, a.vscales);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers (called by the C ABI after validation).
 // ---------------------------------------------------------------------------
 hipError_t launch_calib_absmax(const void* q, const void* k, int64_t B, int64_t Hq, int64_t Hkv,
@@ -168,18 +211,48 @@ hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_quant_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d,
-                          uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  const int64_t Npad = pad_tokens(N);
-  const int64_t tiles = B * H * (Npad / 64);
-  if (tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)tiles), block(256);
-  const uint16_t* vv = (const uint16_t*)v;
+hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const float* inv_s,
+                            const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q,
+                            int64_t N_kv, int64_t d, uint8_t* q_codes, uint8_t* q_scales,
+                            uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                            uint8_t* v_scales, hipStream_t stream) {
+  if (d != 64 && d != 128 && d != 256) {  // Q / K only (V needs one of these d)
+    hipError_t e = hipSuccess;
+    if (q) e = launch_quant_rows(q, s, B, Hq, Hkv, N_q, d, q_codes, q_scales, stream);
+    if (e == hipSuccess && k) e = launch_quant_rows(k, inv_s, B, Hkv, Hkv, N_kv, d, k_codes, k_scales, stream);
+    return e;
+  }
+  QuantArgs a;
+  const void* xs[2] = {q, k};
+  const float* ms[2] = {s, inv_s};
+  const int64_t Hs[2] = {Hq, Hkv}, Ns[2] = {N_q, N_kv};
+  uint8_t* cs[2] = {q_codes, k_codes};
+  uint8_t* ss[2] = {q_scales, k_scales};
+  for (int i = 0; i < 2; i++) {
+    a.x[i] = (const uint16_t*)xs[i];
+    a.mult[i] = ms[i];
+    a.H[i] = Hs[i];
+    a.G[i] = Hs[i] / Hkv;
+    a.N[i] = Ns[i];
+    a.Npad[i] = pad_tokens(Ns[i]);
+    a.threads[i] = xs[i] ? B * Hs[i] * a.Npad[i] * (d / 32) : 0;
+    a.blocks[i] = (a.threads[i] + 255) / 256;
+    a.codes[i] = cs[i];
+    a.scales[i] = ss[i];
+  }
+  a.v = (const uint16_t*)v;
+  a.vN = N_kv;
+  a.vNpad = pad_tokens(N_kv);
+  a.vcodes = v_codes;
+  a.vscales = v_scales;
+  const int64_t vtiles = v ? B * Hkv * (a.vNpad / 64) : 0;
+  const int64_t blocks = a.blocks[0] + a.blocks[1] + vtiles;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(256);
   switch (d) {
-    case 64: quant_v_kernel<64><<<grid, block, 0, stream>>>(vv, N, Npad, codes, scales); break;
-    case 128: quant_v_kernel<128><<<grid, block, 0, stream>>>(vv, N, Npad, codes, scales); break;
-    case 256: quant_v_kernel<256><<<grid, block, 0, stream>>>(vv, N, Npad, codes, scales); break;
-    default: return hipErrorInvalidValue;
+    case 64: quant_qkv_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    case 128: quant_qkv_kernel<128><<<grid, block, 0, stream>>>(a); break;
+    default: quant_qkv_kernel<256><<<grid, block, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }
