@@ -23,7 +23,7 @@
 //  * Prefill: a workgroup is 4 wavefronts that read the same KV head (the
 //    heads of one GQA group, or consecutive row blocks of one head); each
 //    K_hat/V_hat tile is loaded once per workgroup with 1 KB-contiguous
-//    loads and staged through double-buffered LDS in the MFMA operand order
+//    direct global-to-LDS copies into double-buffered stages in MFMA operand order
 //    (a lane reads its operand as one conflict-free 16-byte LDS load).  The
 //    grid's fastest dimension is the KV head, so the round-robin dispatch over
 //    the 8 XCDs keeps each KV head's tiles in one L2.
@@ -303,23 +303,24 @@ struct Stage {
   static constexpr int BYTES = VSC_OFF + VSC_BYTES;
   static constexpr int N_KC = NB * KS;   // 1 KB pieces of K_hat codes
   static constexpr int N_VC = NU * CT;   // 1 KB pieces of V_hat codes
-  // every wave copies CODE_PER_WAVE code pieces and SC_UNITS 16-byte units of
-  // the scale bytes (a quarter of them): the same compile-time work per wave
-  static constexpr int CODE_PER_WAVE = (N_KC + N_VC) / 4;
-  static constexpr int SC_UNITS = (KSC_BYTES + VSC_BYTES) / 16 / 4;
-  static constexpr int PER_WAVE = CODE_PER_WAVE + 1;
-  static_assert((N_KC + N_VC) % 4 == 0, "code pieces split evenly over 4 waves");
-  static_assert(SC_UNITS >= 1 && SC_UNITS <= 64, "scale bytes fit one load per wave");
+  // 16-byte units of scale bytes (K_hat then V_hat, one contiguous LDS range)
+  static constexpr int SCU = (KSC_BYTES + VSC_BYTES) / 16;
+  // per wave: CPW code pieces and SCU/4 units of scale bytes
+  static constexpr int CPW = (N_KC + N_VC) / 4;
+  static_assert((N_KC + N_VC) % 4 == 0 && SCU % 4 == 0 && SCU / 4 <= 64, "even split over 4 waves");
 };
 
-// The pieces this wave copies: per-lane source pointers for the tile at key 0
-// (a tile at kb0 adds kb0 * step bytes) and LDS destinations.  Lanes beyond a
-// wave's share of the scale bytes repeat its last unit (same bytes to the same
-// LDS address), so every lane runs the same straight-line copy.
+// Tile copies are direct global -> LDS transfers (global_load_lds_dwordx4):
+// one instruction moves 16 bytes per lane into LDS lane after lane, so 64
+// lanes fill one 1 KB MFMA operand piece of the stage.  Each of the 4
+// wavefronts copies CPW code pieces and a quarter of the scale bytes (its
+// first SCU/4 lanes).  Sources are for the tile at key 0; the tile at kb0
+// adds kb0 * D/2 bytes to a code source (K_hat rows and 64-token V_hat tiles
+// alike) and kb0 * D/32 to a scale source.
 template <int D, int KT>
-struct StagePlan {
-  const uint8_t* src[Stage<D, KT>::PER_WAVE];
-  int dst[Stage<D, KT>::PER_WAVE];
+struct DmaPlan {
+  const uint8_t* src[Stage<D, KT>::CPW + 1];  // per lane; the last one is the scale unit
+  int dst[Stage<D, KT>::CPW + 1];             // LDS offset in the stage (wave-uniform)
 };
 
 struct KvBases {
@@ -329,49 +330,46 @@ struct KvBases {
   const uint8_t* vs;  // V_hat scales: [Npad/64][D][2]
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <int D, int KT>
-__device__ __forceinline__ void make_plan(const KvBases& kv, StagePlan<D, KT>& pl) {
+__device__ __forceinline__ void make_dma_plan(const KvBases& kv, DmaPlan<D, KT>& pl) {
   using S = Stage<D, KT>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 #pragma unroll
-  for (int j = 0; j < S::CODE_PER_WAVE; j++) {
-    const int i = wave + 4 * j;  // code piece index
+  for (int j = 0; j < S::CPW; j++) {
+    const int i = wave + 4 * j;
     if (i < S::N_KC) {
-      const int b = i / S::KS, s = i % S::KS;
-      pl.src[j] = kv.kc + (32 * b + l32) * (D / 2) + (2 * s + hf) * 16;
-      pl.dst[j] = S::KC_OFF + i * 1024 + lane * 16;
+      const int b = i / S::KS, sk = i % S::KS;
+      pl.src[j] = kv.kc + (32 * b + l32) * (D / 2) + (2 * sk + hf) * 16;
+      pl.dst[j] = S::KC_OFF + i * 1024;
     } else {
       const int jj = i - S::N_KC, u = jj / S::CT, ct = jj % S::CT;
       pl.src[j] = kv.vc + (u * D + 32 * ct + l32) * 32 + 16 * hf;
-      pl.dst[j] = S::VC_OFF + jj * 1024 + lane * 16;
+      pl.dst[j] = S::VC_OFF + jj * 1024;
     }
   }
-  const int k = wave * S::SC_UNITS + (lane < S::SC_UNITS ? lane : S::SC_UNITS - 1);
-  const bool kside = k * 16 < S::KSC_BYTES;
-  const int kk = k - S::KSC_BYTES / 16;
-  pl.src[S::CODE_PER_WAVE] = kside ? kv.ks + k * 16 : kv.vs + kk * 16;
-  pl.dst[S::CODE_PER_WAVE] = kside ? S::KSC_OFF + k * 16 : S::VSC_OFF + kk * 16;
+  constexpr int KU = S::KSC_BYTES / 16;
+  const int k = wave * (S::SCU / 4) + lane;  // scale unit of this lane (lanes < SCU/4)
+  pl.src[S::CPW] = k < KU ? kv.ks + k * 16 : kv.vs + (k - KU) * 16;
+  pl.dst[S::CPW] = S::KSC_OFF + wave * (S::SCU / 4) * 16;
 }
 
+// Issue this wave's copies of the tile at kb0 into `stage`.  Completion is
+// awaited by the workgroup barrier that ends the iteration (its memory fence
+// waits for outstanding vector memory operations).
 template <int D, int KT>
-__device__ __forceinline__ void stage_load(const StagePlan<D, KT>& pl, int kb0,
-                                           u32x4 (&reg)[Stage<D, KT>::PER_WAVE]) {
+__device__ __forceinline__ void dma_tile(const DmaPlan<D, KT>& pl, int kb0, uint8_t* stage) {
   using S = Stage<D, KT>;
 #pragma unroll
-  for (int j = 0; j < S::CODE_PER_WAVE; j++)
-    reg[j] = *reinterpret_cast<const u32x4*>(pl.src[j] + (int64_t)kb0 * (D / 2));
-  reg[S::CODE_PER_WAVE] =
-      *reinterpret_cast<const u32x4*>(pl.src[S::CODE_PER_WAVE] + (int64_t)kb0 * (D / 32));
-}
-
-template <int D, int KT>
-__device__ __forceinline__ void stage_store(uint8_t* stage, const StagePlan<D, KT>& pl,
-                                            const u32x4 (&reg)[Stage<D, KT>::PER_WAVE]) {
-#pragma unroll
-  for (int j = 0; j < Stage<D, KT>::PER_WAVE; j++)
-    *reinterpret_cast<u32x4*>(stage + pl.dst[j]) = reg[j];
+  for (int j = 0; j < S::CPW; j++)
+    __builtin_amdgcn_global_load_lds((const void*)(pl.src[j] + (int64_t)kb0 * (D / 2)),
+                                     (lds_ptr_t)(stage + pl.dst[j]), 16, 0, 0);
+  if ((threadIdx.x & 63) < S::SCU / 4)
+    __builtin_amdgcn_global_load_lds((const void*)(pl.src[S::CPW] + (int64_t)kb0 * (D / 32)),
+                                     (lds_ptr_t)(stage + pl.dst[S::CPW]), 16, 0, 0);
 }
 
 // V_hat operands read from an LDS stage.
@@ -396,7 +394,10 @@ template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   using S = Stage<D, KT>;
   constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BYTES];
+  // two stages as separate arrays, so that reads of one are not ordered
+  // behind the copies in flight into the other
+  __shared__ __attribute__((aligned(16))) uint8_t st0[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[S::BYTES];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int nh = p.heads_per_wg, nr = 4 / nh;
@@ -452,28 +453,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     }
   }
 
-  // Copy pipeline: the bytes of tile t+1 are loaded into registers right after
-  // the barrier that ends tile t-1, written to the free LDS stage after tile
-  // t's compute, and published by the barrier that ends tile t.  Each load is
-  // thus in flight across a whole tile of compute (and, crossing the loop's
-  // back edge, cannot be sunk to its use).  Loads past the last tile re-read
-  // the last tile (in bounds; never read back).
-  StagePlan<D, KT> plan;
-  make_plan<D, KT>(kv, plan);
-  const int last_kb0 = (tiles - 1) * KT;
-  u32x4 stage_reg[S::PER_WAVE];
-  stage_load<D, KT>(plan, 0, stage_reg);
-  stage_store<D, KT>(smem, plan, stage_reg);
-  stage_load<D, KT>(plan, tiles > 1 ? KT : 0, stage_reg);
+  // Copy pipeline: tile t+1 is copied into the free stage right after the
+  // barrier that ended tile t-1 (the last reads of that stage), so the copy
+  // runs under tile t's compute; the barrier that ends tile t waits for it.
+  DmaPlan<D, KT> plan;
+  make_dma_plan<D, KT>(kv, plan);
+  dma_tile<D, KT>(plan, 0, st0);
   __syncthreads();
 
   v16f accO[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
   float m = kNegInf, l = 0.0f;
-  for (int t = 0; t < tiles; t++) {
+  auto step = [&](int t, const uint8_t* st, uint8_t* nxt) {
     const int kb0 = t * KT;
-    const uint8_t* st = smem + (t & 1) * S::BYTES;
+    if (t + 1 < tiles) dma_tile<D, KT>(plan, kb0 + KT, nxt);
     if (wave_active && kb0 <= wave_last_key) {
       v16f sacc[NB];
 #pragma unroll
@@ -490,10 +484,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
       LdsV<D, KT> vops{st};
       softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
     }
-    stage_store<D, KT>(smem + ((t + 1) & 1) * S::BYTES, plan, stage_reg);
     __syncthreads();
-    const int kb2 = kb0 + 2 * KT;
-    stage_load<D, KT>(plan, kb2 <= last_kb0 ? kb2 : last_kb0, stage_reg);
+  };
+  for (int t = 0; t < tiles; t += 2) {
+    step(t, st0, st1);
+    if (t + 1 < tiles) step(t + 1, st1, st0);
   }
 
   if (wave_active && qrow < p.N_q) store_out<D>(p.out + (bh * p.N_q + qrow) * D, accO, l);
