@@ -23,7 +23,7 @@
 //  * Prefill: a workgroup is 4 wavefronts that read the same KV head (the
 //    heads of one GQA group, or consecutive row blocks of one head); each
 //    K_hat/V_hat tile is loaded once per workgroup with 1 KB-contiguous
-//    direct global-to-LDS copies into double-buffered stages in MFMA operand order
+//    direct global-to-LDS copies into a three-stage ring in MFMA operand order
 //    (a lane reads its operand as one conflict-free 16-byte LDS load).  The
 //    grid's fastest dimension is the KV head, so the round-robin dispatch over
 //    the 8 XCDs keeps each KV head's tiles in one L2.
@@ -394,10 +394,11 @@ template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   using S = Stage<D, KT>;
   constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
-  // two stages as separate arrays, so that reads of one are not ordered
-  // behind the copies in flight into the other
+  // three stages as separate arrays, so that reads of one are not ordered
+  // behind the copies in flight into another
   __shared__ __attribute__((aligned(16))) uint8_t st0[S::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t st1[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[S::BYTES];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int nh = p.heads_per_wg, nr = 4 / nh;
@@ -453,42 +454,52 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     }
   }
 
-  // Copy pipeline: tile t+1 is copied into the free stage right after the
-  // barrier that ended tile t-1 (the last reads of that stage), so the copy
-  // runs under tile t's compute; the barrier that ends tile t waits for it.
+  // Pipeline over three LDS stages.  Iteration t: copy tile t+2 into the
+  // stage that held tile t-1 (free since the barrier that ended iteration
+  // t-1), run the softmax and PV of tile t (its S^T was computed at the end of
+  // iteration t-1), then issue the S^T MFMAs of tile t+1 -- they execute
+  // while the wave waits at the barrier that ends the iteration, which also
+  // waits for this wave's copies to land.
   DmaPlan<D, KT> plan;
   make_dma_plan<D, KT>(kv, plan);
   dma_tile<D, KT>(plan, 0, st0);
+  if (tiles > 1) dma_tile<D, KT>(plan, KT, st1);
   __syncthreads();
 
   v16f accO[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
   float m = kNegInf, l = 0.0f;
-  auto step = [&](int t, const uint8_t* st, uint8_t* nxt) {
+  auto computes = [&](int t) { return wave_active && t < tiles && t * KT <= wave_last_key; };
+  v16f sacc[NB];
+  auto scores = [&](const uint8_t* st) {
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) {
+      uint4 ka[KS];
+#pragma unroll
+      for (int s = 0; s < KS; s++)
+        ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
+      uint32_t ksw[SW];
+      row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
+      sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
+    }
+  };
+  if (computes(0)) scores(st0);
+  auto step = [&](int t, const uint8_t* cur, const uint8_t* nxt, uint8_t* fill) {
     const int kb0 = t * KT;
-    if (t + 1 < tiles) dma_tile<D, KT>(plan, kb0 + KT, nxt);
-    if (wave_active && kb0 <= wave_last_key) {
-      v16f sacc[NB];
-#pragma unroll
-      for (int bb = 0; bb < NB; bb++) {
-        uint4 ka[KS];
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-          ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
-        uint32_t ksw[SW];
-        row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
-        sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
-      }
+    if (t + 2 < tiles) dma_tile<D, KT>(plan, kb0 + 2 * KT, fill);
+    if (computes(t)) {
       const bool need_mask = (kb0 + KT - 1) > wave_lim;
-      LdsV<D, KT> vops{st};
+      LdsV<D, KT> vops{cur};
       softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
     }
+    if (computes(t + 1)) scores(nxt);
     __syncthreads();
   };
-  for (int t = 0; t < tiles; t += 2) {
-    step(t, st0, st1);
-    if (t + 1 < tiles) step(t + 1, st1, st0);
+  for (int t = 0; t < tiles; t += 3) {
+    step(t, st0, st1, st2);
+    if (t + 1 < tiles) step(t + 1, st1, st2, st0);
+    if (t + 2 < tiles) step(t + 2, st2, st0, st1);
   }
 
   if (wave_active && qrow < p.N_q) store_out<D>(p.out + (bh * p.N_q + qrow) * D, accO, l);
