@@ -718,20 +718,35 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   if (t >= rows * q) return;
   const int64_t row = t / q;
   const int c4 = (int)(t % q);
-  const float* ml = ws_ml + row * C * 2;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml + row * C * 2);
   float M = kNegInf;
-  for (int k = 0; k < C; k++) M = fmaxf(M, ml[2 * k]);
+  for (int k = 0; k < C; k++) M = fmaxf(M, ml[k].x);
   float L = 0.0f;
   float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k = 0; k < C; k++) {
-    const float mk = ml[2 * k];
-    const float w = (mk == kNegInf) ? 0.0f : exp2_hw(mk - M);
-    const float wl = w * ml[2 * k + 1];
-    L = L + wl;
-    const float4 o = *reinterpret_cast<const float4*>(ws_o + (row * C + k) * d + 4 * c4);
-    const float wo[4] = {w * o.x, w * o.y, w * o.z, w * o.w};
+  // partials in groups of 8: the group's loads are all issued before its
+  // (in-order) accumulation
+  constexpr int GRP = 8;
+  for (int k0 = 0; k0 < C; k0 += GRP) {
+    float4 o[GRP];
+    float2 st[GRP];
 #pragma unroll
-    for (int i = 0; i < 4; i++) A[i] = A[i] + wo[i];
+    for (int j = 0; j < GRP; j++) {
+      if (k0 + j < C) {
+        o[j] = *reinterpret_cast<const float4*>(ws_o + (row * C + k0 + j) * d + 4 * c4);
+        st[j] = ml[k0 + j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GRP; j++) {
+      if (k0 + j < C) {
+        const float w = (st[j].x == kNegInf) ? 0.0f : exp2_hw(st[j].x - M);
+        const float wl = w * st[j].y;
+        L = L + wl;
+        const float wo[4] = {w * o[j].x, w * o[j].y, w * o[j].z, w * o[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) A[i] = A[i] + wo[i];
+      }
+    }
   }
   const float lf = round_f16(L);
   const uint32_t lo = (uint32_t)float_to_half_bits(A[0] / lf) | ((uint32_t)float_to_half_bits(A[1] / lf) << 16);
