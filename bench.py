@@ -175,33 +175,55 @@ def row_flops(w, rows):
     return float(np.sum(4.0 * w.d * keys))
 
 
-def parity_sample(w, hf, st, rows, reorder=True):
-    """Oracle on sampled rows vs the GPU output of the timed launch configuration."""
-    import oracle
-    s_ref = inv_ref = None
-    if w.smooth:
-        s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
-    rq = oracle.quantize_rows(w.q, w.Hkv, s_ref)
-    rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
-    rv = oracle.quantize_v(w.v)
-    ref = oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=int(reorder),
-                      kv_tile=default_kv_tile(w.d), q4=rq, k4=rk, v4=rv, rows=rows)
-    got = st["out"].reshape(-1, w.d)[rows].cpu().numpy().astype(np.float64)
-    exp = ref["out"].view(np.float16).astype(np.float64)
-    rowmax = np.abs(exp).max(axis=1, keepdims=True)
-    e = np.abs(got - exp) / rowmax
-    # error of the 4-bit path against fp64 softmax attention on the binary16 inputs
-    exact = oracle.attn_exact(w.q, w.k, w.v, w.causal, rows=rows)
-    ex_max = np.abs(exact).max(axis=1, keepdims=True)
-    ee = np.abs(got - exact) / ex_max
-    return float(e.max()), float(e.mean()), float(ee.max()), float(ee.mean())
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
-def cpu_baseline(w, target_s=12.0, seed=777):
-    """The oracle's attention forward (quantized operands given) on a seeded sample of query
-    rows, on the host threads this process may use (at most 16).  A first 1024-row pass sizes
-    the sample so that the timed pass takes about `target_s` seconds."""
+def phat_tile_sums(codes, scales, kv_tile):
+    """Sum of P_hat per (row, tile) from a dumped [rows][Npad/2] codes / [rows][Npad/32] scales
+    pair: E2M1 value (sign in bit 3) times 2^(scale byte - 127) per 32-key block."""
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
+    val = E2M1_MAGNITUDES[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    blk = val.reshape(codes.shape[0], -1, 32).sum(axis=2) * np.exp2(scales.astype(np.float64) - 127)
+    return blk.reshape(codes.shape[0], -1, kv_tile // 32).sum(axis=2)
+
+
+def eps_bar_gpu_dump(w, hf, torch, heads, kv_tile=64):
+    """GPU half of the epsilon-bar diagnostic: one P_hat-dumping launch of the whole workload
+    (off the timed path); returns the dumped rows of the sampled (b, h) heads."""
+    st = prepare_prefill(w, hf, torch)
+    q4, k4, v4 = st["bufs"]
+    hf.quantize_qkv(st["q"], st["k"], st["v"], Hkv=w.Hkv, smooth=w.smooth, s=st["s"],
+                    inv_s=st["inv"], out=st["bufs"])
+    total = w.B * w.Hq * w.N_q
+    npk = (w.N_kv + 127) // 128 * 128
+    phat = hf.MX4(torch.zeros((total, npk // 2), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((total, npk // 32), dtype=torch.uint8, device="cuda"))
+    hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
+                causal=w.causal, smooth=w.smooth, reorder=True, out=st["out"], kv_tile=kv_tile,
+                phat=phat)
+    rows = (heads[:, None] * w.N_q + np.arange(w.N_q)[None, :]).reshape(-1)
+    idx = torch.from_numpy(rows).cuda()
+    codes, scales = phat.codes[idx].cpu().numpy(), phat.scales[idx].cpu().numpy()
+    del st, phat
+    torch.cuda.empty_cache()
+    return rows, codes, scales
+
+
+def cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0=None, target_s=12.0, seed=777):
+    """Everything that runs the CPU oracle, after the GPU measurements:
+
+    * the baseline: the oracle's attention forward (quantized operands given, same tile
+      size as the GPU) on a seeded sample of query rows of the primary workload, on the host
+      threads this process may use (at most 16); a first 1024-row pass sizes the sample so
+      that the timed pass takes about `target_s` seconds;
+    * parity of the GPU output on those rows (error relative to each row's max |O_oracle|)
+      and the error of both against fp64 softmax attention on the binary16 inputs (also for
+      the GPU output with P-Reordering off, when given);
+    * the epsilon-bar diagnostic: per tile of 64 query rows x 64 keys, the mean over its rows
+      of (sum P_hat - sum P) / sum P, from the oracle's per-tile sums on sampled heads, with
+      the GPU's dumped P_hat checked to give the same sum P_hat."""
     import oracle
+    res = {}
     s_ref = inv_ref = None
     if w.smooth:
         s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
@@ -210,19 +232,82 @@ def cpu_baseline(w, target_s=12.0, seed=777):
     rv = oracle.quantize_v(w.v)
     threads = max(1, min(16, os.cpu_count() or 1))
     total = w.B * w.Hq * w.N_q
+    kt = default_kv_tile(w.d)
 
     def timed(rows):
         t0 = time.perf_counter()
-        oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=1,
-                    kv_tile=default_kv_tile(w.d), q4=rq, k4=rk, v4=rv, rows=rows, threads=threads)
-        return time.perf_counter() - t0
+        r = oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=1,
+                        kv_tile=kt, q4=rq, k4=rk, v4=rv, rows=rows, threads=threads)
+        return time.perf_counter() - t0, r
 
     probe = sample_rows(w, 1024, seed=seed + 1)
-    rate = row_flops(w, probe) / timed(probe)
+    dt0, _ = timed(probe)
+    rate = row_flops(w, probe) / dt0
     n = int(min(total, max(1024, 1024 * target_s * rate / row_flops(w, probe))))
     rows = sample_rows(w, n, seed=seed)
-    dt = timed(rows)
-    return row_flops(w, rows) / dt / 1e12, dt, threads, len(rows)
+    dt, ref = timed(rows)
+    res["cpu_baseline"] = {
+        "value": row_flops(w, rows) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{w.name} attention (quantized operands given, kv_tile {kt}), {len(rows)} "
+                  f"seeded random query rows of {total}, {dt:.1f} s"}
+
+    got = gpu_out.reshape(-1, w.d)[rows].astype(np.float64)
+    exp = ref["out"].view(np.float16).astype(np.float64)
+    e = np.abs(got - exp) / np.abs(exp).max(axis=1, keepdims=True)
+    sub = rows[:256]
+    exact = oracle.attn_exact(w.q, w.k, w.v, w.causal, rows=sub, threads=threads)
+    ex_max = np.abs(exact).max(axis=1, keepdims=True)
+    eg = np.abs(got[:256] - exact) / ex_max
+    eo = np.abs(exp[:256] - exact) / ex_max
+    res["parity_sample"] = {
+        "rows": len(rows), "err_max": float(e.max()), "err_mean": float(e.mean()),
+        "vs_fp64_exact_rows": len(sub), "gpu_vs_fp64_exact_max": float(eg.max()),
+        "gpu_vs_fp64_exact_mean": float(eg.mean()), "oracle_vs_fp64_exact_max": float(eo.max()),
+        "oracle_vs_fp64_exact_mean": float(eo.mean())}
+    if gpu_out_r0 is not None:
+        e0 = np.abs(gpu_out_r0.reshape(-1, w.d)[sub].astype(np.float64) - exact) / ex_max
+        res["parity_sample"]["gpu_reorder_off_vs_fp64_exact_max"] = float(e0.max())
+        res["parity_sample"]["gpu_reorder_off_vs_fp64_exact_mean"] = float(e0.mean())
+
+    if eps_inputs is not None:
+        we, erows, codes, scales = eps_inputs
+        s2 = i2 = None
+        if we.smooth:
+            s2, i2 = oracle.calibrate(we.q_cal, we.k_cal, we.alpha)
+        q2 = oracle.quantize_rows(we.q, we.Hkv, s2)
+        k2 = oracle.quantize_rows(we.k, we.Hkv, i2)
+        v2 = oracle.quantize_v(we.v)
+        r2 = oracle.attn(we.B, we.Hq, we.Hkv, we.N_q, we.N_kv, we.d, causal=we.causal, reorder=1,
+                         kv_tile=64, q4=q2, k4=k2, v4=v2, rows=erows, want_sums=True,
+                         threads=threads)
+        sp, sph = r2["sum_p"], r2["sum_phat"]
+        T = sp.shape[1]
+        gph = phat_tile_sums(codes, scales, 64)[:, :T]
+        seen = np.isfinite(sph)
+        dev = np.abs(gph[seen] - sph[seen]) / np.maximum(sph[seen], 1e-300)
+        valid = seen & (sp > 0)
+        nh = len(erows) // we.N_q
+        shape = (nh, we.N_q // 64, 64, T)
+        spv = np.where(valid, sp, 0.0).reshape(shape)
+        sphv = np.where(valid, sph, 0.0).reshape(shape)
+        val = valid.reshape(shape)
+        eps = np.where(val, (sphv - spv) / np.where(val, spv, 1.0), 0.0)
+        cnt = val.sum(axis=2)
+        tiles = cnt > 0
+        eb = (eps.sum(axis=2) / np.maximum(cnt, 1))[tiles]
+        mw = ((sphv - spv).sum(axis=2) / np.maximum(spv.sum(axis=2), 1e-300))[tiles]
+        hist, edges = np.histogram(eb, bins=16, range=(-0.2, 0.2))
+        res["eps_bar"] = {
+            "workload": f"{we.name}: {nh} seeded (b, h) heads of {we.B * we.Hq}, tiles of 64 rows "
+                        f"x 64 keys", "tiles": int(tiles.sum()),
+            "median": float(np.median(eb)), "mean": float(eb.mean()),
+            "p10": float(np.percentile(eb, 10)), "p90": float(np.percentile(eb, 90)),
+            "fraction_negative": float(np.mean(eb < 0)), "mass_weighted_median": float(np.median(mw)),
+            "histogram": {"edges": [round(x, 4) for x in edges.tolist()], "counts": hist.tolist(),
+                          "below": int(np.sum(eb < -0.2)), "above": int(np.sum(eb > 0.2))},
+            "gpu_dump_sum_phat_max_rel_dev": float(dev.max()) if dev.size else 0.0}
+    return res
 
 
 def main():
@@ -291,18 +376,16 @@ def main():
                      "traffic": traffic, "kernel_ms": round(attn_ms, 5)},
     }
     extra = {}
+    gpu_out = None if a.no_cpu else st["out"].reshape(-1, w.d).cpu().numpy()
+    del st
+    eps_inputs = gpu_out_r0 = None
     if not a.quick:
-        rows = sample_rows(w, 256)
-        emax, emean, xmax, xmean = parity_sample(w, hf, st, rows, reorder=True)
-        extra["parity_sample"] = {"rows": len(rows), "err_max": emax, "err_mean": emean,
-                                  "vs_fp64_exact_max": xmax, "vs_fp64_exact_mean": xmean}
-        log(f"[bench] parity on {len(rows)} sampled rows: max {emax:.2e} mean {emean:.2e}; "
-            f"vs fp64 exact attention: max {xmax:.2e} mean {xmean:.2e}")
-        del st
         ms0, attn0, st0 = run_prefill(w, hf, torch, a.steps, a.warmup, reorder=False)
         extra["qwen3_8b_reorder_off"] = {"ms_per_step": ms0, "attn_ms": attn0,
                                          "attn_tflops": w.flops / (attn0 * 1e-3) / 1e12}
         log(f"[bench] reorder off: attention {attn0:.4f} ms")
+        if not a.no_cpu:
+            gpu_out_r0 = st0["out"].reshape(-1, w.d).cpu().numpy()
         del st0
         for name, fn in (("gemma2_9b_prefill", synth.gemma2_9b),
                          ("llama_batched_prefill", synth.llama_batched)):
@@ -317,6 +400,9 @@ def main():
                 log(f"[bench] {key}: step {msx:.4f} ms, attention {attnx:.4f} ms "
                     f"({extra[key]['attn_tflops']:.1f} TFLOP/s)")
                 del stx
+            if name.startswith("llama") and not a.no_cpu:
+                heads = np.sort(np.random.default_rng(4242).choice(wx.B * wx.Hq, 16, replace=False))
+                eps_inputs = (wx,) + eps_bar_gpu_dump(wx, hf, torch, heads)
         wd = synth.decode()
         msd, attnd, std = run_decode(wd, hf, torch, a.steps, a.warmup)
         gbs = wd.kv_bytes / (attnd * 1e-3) / 1e9
@@ -327,12 +413,19 @@ def main():
         del std
         torch.cuda.empty_cache()
     if not a.no_cpu:
-        tf, dt, thr, nrows = cpu_baseline(w)
-        result["cpu_baseline"] = {"value": tf, "unit": "TFLOP/s", "cores": thr, "kind": "oracle",
-                                  "sample": f"qwen3_8b_prefill attention (quantized operands given), "
-                                            f"{nrows} seeded random query rows of "
-                                            f"{w.B * w.Hq * w.N_q}, {dt:.1f} s"}
-        log(f"[bench] cpu oracle: {tf:.6f} TFLOP/s on {thr} threads ({dt:.1f} s)")
+        cl = cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0)
+        result["cpu_baseline"] = cl.pop("cpu_baseline")
+        log(f"[bench] cpu oracle: {result['cpu_baseline']['value']:.6f} TFLOP/s on "
+            f"{result['cpu_baseline']['cores']} threads ({result['cpu_baseline']['sample']})")
+        ps = cl["parity_sample"]
+        log(f"[bench] parity on {ps['rows']} sampled rows: max {ps['err_max']:.2e} mean "
+            f"{ps['err_mean']:.2e}; vs fp64 exact attention (GPU): max "
+            f"{ps['gpu_vs_fp64_exact_max']:.2e} mean {ps['gpu_vs_fp64_exact_mean']:.2e}")
+        if "eps_bar" in cl:
+            eb = cl["eps_bar"]
+            log(f"[bench] eps_bar over {eb['tiles']} tiles: median {eb['median']:.4f}, "
+                f"{100 * eb['fraction_negative']:.1f} % negative")
+        extra.update(cl)
     if extra:
         result["extra"] = extra
     print(json.dumps(result), flush=True)
