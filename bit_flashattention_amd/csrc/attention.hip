@@ -555,26 +555,36 @@ __device__ __forceinline__ void reg_load_v(const KvBases& kv, int kb0, RegOps<D,
   }
 }
 
-template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
-__global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
-  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
-  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t total = p.B * p.Hkv * p.num_splits;
-  if (wid >= total) return;
-  const int chunk = (int)(wid % p.num_splits);
-  const int64_t bg = wid / p.num_splits;
-  const int64_t b = bg / p.Hkv, g = bg % p.Hkv;
+// The query operand of a split / decode wavefront: its 32 MFMA columns are the
+// G * N_q (head-in-group j, row i) pairs of KV head (b, g), column q = j * N_q + i
+// (columns >= G * N_q are zero).  With QRAW the binary16 query is smoothed and
+// quantized here exactly as the quantization kernel does it.
+struct SplitCols {
+  bool real;
+  int64_t row;  // flat query row (b*Hq + h)*N_q + i of this lane's column
+  int64_t i;    // query index within the sequence
+};
 
+__device__ __forceinline__ SplitCols split_cols(const KParams& p, int64_t b, int64_t g) {
+  const int l32 = threadIdx.x & 31;
   const int cols = p.G * (int)p.N_q;
-  const bool real = l32 < cols;
-  const int j = real ? l32 / (int)p.N_q : 0;  // head within the group
-  const int64_t i = real ? l32 % p.N_q : p.N_q - 1;
+  SplitCols c;
+  c.real = l32 < cols;
+  const int j = c.real ? l32 / (int)p.N_q : 0;  // head within the group
+  c.i = c.real ? l32 % p.N_q : p.N_q - 1;
   const int64_t h = g * p.G + j;
-  const int64_t row = (b * p.Hq + h) * p.N_q + i;  // flat query row
+  c.row = (b * p.Hq + h) * p.N_q + c.i;
+  return c;
+}
 
-  uint4 qb[KS];
-  uint32_t qsc[SW];
+template <int D, bool QRAW>
+__device__ __forceinline__ void split_query(const KParams& p, int64_t b, int64_t g, const SplitCols& cs,
+                                            uint4 (&qb)[D / 64], uint32_t (&qsc)[(D / 64 + 1) / 2]) {
+  constexpr int KS = D / 64, SW = (D / 64 + 1) / 2;
+  const int hf = (threadIdx.x >> 5) & 1;
+  const bool real = cs.real;
+  const int64_t row = cs.row, i = cs.i;
+  const int64_t h = (row / p.N_q) % p.Hq;  // row = (b*Hq + h)*N_q + i
 #pragma unroll
   for (int w = 0; w < SW; w++) qsc[w] = 0u;
   if constexpr (QRAW) {
@@ -623,6 +633,29 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
       qb[s] = real ? *reinterpret_cast<const uint4*>(qr + (2 * s + hf) * 16) : make_uint4(0, 0, 0, 0);
     if (real) row_scales<D>(p.q_scales + qr_idx * (D / 32), hf, qsc);
   }
+}
+
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
+__global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
+  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = p.B * p.Hkv * p.num_splits;
+  if (wid >= total) return;
+  const int chunk = (int)(wid % p.num_splits);
+  const int64_t bg = wid / p.num_splits;
+  const int64_t b = bg / p.Hkv, g = bg % p.Hkv;
+
+  const int cols = p.G * (int)p.N_q;
+  const bool real = l32 < cols;
+  const int j = real ? l32 / (int)p.N_q : 0;  // head within the group
+  const int64_t i = real ? l32 % p.N_q : p.N_q - 1;
+  const int64_t h = g * p.G + j;
+  const int64_t row = (b * p.Hq + h) * p.N_q + i;  // flat query row
+
+  uint4 qb[KS];
+  uint32_t qsc[SW];
+  split_query<D, QRAW>(p, b, g, SplitCols{real, row, i}, qb, qsc);
 
   KvBases kv;
   kv.kc = p.k_codes + bg * p.Npad_kv * (D / 2);
@@ -705,6 +738,146 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-KV with the merge fused in (decode).  One workgroup per KV head (b, g):
+// wave w runs chunks w, w+4, w+8, ... one after another (each from
+// (-inf, 0, 0), streaming its tiles through the same register ring as the
+// split kernel), and leaves each chunk's (m, l, O) of its real columns in
+// LDS.  After a barrier the workgroup merges the C partials in chunk order --
+// the same arithmetic as attn_merge_kernel -- and writes the output.  No
+// partial state leaves the chip.  LDS: C * cols * (D + 2) floats.
+// ---------------------------------------------------------------------------
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
+__global__ __launch_bounds__(256, (D * KT <= 128 * 64) ? 2 : 1) void attn_decode_kernel(KParams p) {
+  constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
+  extern __shared__ __attribute__((aligned(16))) float part[];
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = threadIdx.x >> 6;
+  const int64_t bg = blockIdx.x;
+  const int64_t b = bg / p.Hkv, g = bg % p.Hkv;
+  const int C = p.num_splits, tpc = p.tiles_per_split, T = p.n_tiles;
+  const int cols = p.G * (int)p.N_q;
+  float* part_o = part;                       // [C][cols][D]
+  float* part_ml = part + (int64_t)C * cols * D;  // [C][cols][2]
+
+  const SplitCols cs = split_cols(p, b, g);
+  uint4 qb[KS];
+  uint32_t qsc[SW];
+  split_query<D, QRAW>(p, b, g, cs, qb, qsc);
+
+  KvBases kv;
+  kv.kc = p.k_codes + bg * p.Npad_kv * (D / 2);
+  kv.ks = p.k_scales + bg * p.Npad_kv * (D / 32);
+  kv.vc = p.v_codes + bg * p.Npad_kv * (D / 2);
+  kv.vs = p.v_scales + bg * p.Npad_kv * (D / 32);
+
+  const int64_t shift = p.N_kv - p.N_q;
+  const int lim = CAUSAL ? (int)min64(cs.i + shift, p.N_kv - 1) : (int)(p.N_kv - 1);
+  const int wave_lim = CAUSAL ? (int)min64(shift, p.N_kv - 1) : (int)(p.N_kv - 1);
+
+  uint8_t* phc = nullptr;
+  uint8_t* phs = nullptr;
+  if constexpr (DUMP) {
+    if (cs.real) {
+      phc = p.phat_codes + cs.row * (p.Npad_kv / 2);
+      phs = p.phat_scales + cs.row * (p.Npad_kv / 32);
+    }
+  }
+
+  v16f accO[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
+  float m = kNegInf, l = 0.0f;
+  // this wave's positions: chunk k = wave + 4 * (pos / tpc), tile k * tpc + pos % tpc
+  const int nck = wave < C ? (C - wave + 3) / 4 : 0;
+  const int npos = nck * tpc;
+  auto tile_of = [&](int pos) { return (wave + 4 * (pos / tpc)) * tpc + pos % tpc; };
+  if (npos > 0) {
+    RegOps<D, KT> o0, o1, o2;
+    auto kbc = [&](int pos) {
+      const int t = tile_of(pos < npos ? pos : npos - 1);
+      return (t < T ? t : T - 1) * KT;
+    };
+    auto load = [&](RegOps<D, KT>& op, int pos) {
+      reg_load_k<D, KT>(kv, kbc(pos), op);
+      reg_load_v<D, KT>(kv, kbc(pos), op);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step = [&](RegOps<D, KT>& op, int pos) {
+      if (pos < npos) {
+        const int t = tile_of(pos);
+        if (t < T) {
+          const int kb0 = t * KT;
+          v16f sacc[NB];
+#pragma unroll
+          for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(op.ka[bb], op.ksw[bb], qb, qsc);
+          const bool need_mask = (kb0 + KT - 1) > wave_lim;
+          softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, op, accO, m, l, phc, phs);
+        }
+        if (pos % tpc == tpc - 1) {  // chunk done: its state to LDS, then start the next one
+          const int k = wave + 4 * (pos / tpc);
+          if (cs.real) {
+            float* wo = part_o + ((int64_t)k * cols + l32) * D;
+#pragma unroll
+            for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+              for (int r4 = 0; r4 < 4; r4++)
+                *reinterpret_cast<float4*>(wo + 32 * ct + 8 * r4 + 4 * hf) =
+                    make_float4(accO[ct][4 * r4], accO[ct][4 * r4 + 1], accO[ct][4 * r4 + 2],
+                                accO[ct][4 * r4 + 3]);
+            if (hf == 0) {
+              part_ml[((int64_t)k * cols + l32) * 2] = m;
+              part_ml[((int64_t)k * cols + l32) * 2 + 1] = l;
+            }
+          }
+#pragma unroll
+          for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
+          m = kNegInf;
+          l = 0.0f;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load(o0, 0);
+    load(o1, 1);
+    for (int pos = 0; pos < npos; pos += 3) {
+      load(o2, pos + 2);
+      step(o0, pos);
+      load(o0, pos + 3);
+      step(o1, pos + 1);
+      load(o1, pos + 4);
+      step(o2, pos + 2);
+    }
+  }
+  __syncthreads();
+
+  // merge in chunk order: M = max m_k, w_k = 2^(m_k - M), L = sum w_k l_k,
+  // A = sum w_k O_k (fp32, sequential), out = fp16(A / fp16(L))
+  for (int idx = threadIdx.x; idx < cols * (D / 4); idx += 256) {
+    const int q = idx / (D / 4), c4 = idx % (D / 4);
+    float M = kNegInf;
+    for (int k = 0; k < C; k++) M = fmaxf(M, part_ml[((int64_t)k * cols + q) * 2]);
+    float L = 0.0f;
+    float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < C; k++) {
+      const float mk = part_ml[((int64_t)k * cols + q) * 2];
+      const float w = (mk == kNegInf) ? 0.0f : exp2_hw(mk - M);
+      const float wl = w * part_ml[((int64_t)k * cols + q) * 2 + 1];
+      L = L + wl;
+      const float4 o = *reinterpret_cast<const float4*>(part_o + ((int64_t)k * cols + q) * D + 4 * c4);
+      const float wo[4] = {w * o.x, w * o.y, w * o.z, w * o.w};
+#pragma unroll
+      for (int z = 0; z < 4; z++) A[z] = A[z] + wo[z];
+    }
+    const float lf = round_f16(L);
+    const int j = q / (int)p.N_q;
+    const int64_t row = (b * p.Hq + g * p.G + j) * p.N_q + q % (int)p.N_q;
+    const uint32_t lo = (uint32_t)float_to_half_bits(A[0] / lf) | ((uint32_t)float_to_half_bits(A[1] / lf) << 16);
+    const uint32_t hi = (uint32_t)float_to_half_bits(A[2] / lf) | ((uint32_t)float_to_half_bits(A[3] / lf) << 16);
+    *reinterpret_cast<uint2*>(p.out + row * D + 4 * c4) = make_uint2(lo, hi);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split partials, in chunk order: M = max m_k, w_k = 2^(m_k - M),
 // L = sum w_k l_k, A = sum w_k O_k (fp32, sequential), out = fp16(A / fp16(L)).
 // One thread per (row, 4 channels): 16-byte partial loads, 8-byte stores.
@@ -764,8 +937,22 @@ hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// LDS bytes of the fused decode kernel's partial states (0: too large, use the
+// split kernel and the merge kernel).
+inline size_t decode_lds_bytes(const KParams& kp, int d) {
+  const size_t bytes = (size_t)kp.num_splits * kp.G * kp.N_q * (d + 2) * sizeof(float);
+  return bytes <= 64 * 1024 ? bytes : 0;
+}
+
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
 hipError_t launch_split_t(const KParams& kp, hipStream_t stream) {
+  if (kp.num_splits > 1) {
+    if (const size_t lds = decode_lds_bytes(kp, D)) {
+      attn_decode_kernel<D, KT, CAUSAL, REORDER, DUMP, QRAW>
+          <<<dim3((unsigned)(kp.B * kp.Hkv)), dim3(256), lds, stream>>>(kp);
+      return hipGetLastError();
+    }
+  }
   const int64_t waves = kp.B * kp.Hkv * kp.num_splits;
   dim3 grid((unsigned)((waves + 3) / 4));
   attn_split_kernel<D, KT, CAUSAL, REORDER, DUMP, QRAW><<<grid, dim3(256), 0, stream>>>(kp);
