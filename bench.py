@@ -57,28 +57,6 @@ def measured_traffic(kernel: str, flops_per_launch: float):
     return t.get("bytes_per_launch")
 
 
-class Timer:
-    """HIP events on the current stream around each launch of one kernel family."""
-
-    def __init__(self):
-        import torch
-        self.torch = torch
-        self.pairs = []
-
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def stop(self, s):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs.append((s, e))
-
-    def mean_ms(self) -> float:
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else 0.0
-
-
 def prepare_prefill(w, hf, torch):
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, k, v = up(w.q), up(w.k), up(w.v)
@@ -97,31 +75,38 @@ def default_kv_tile(d: int) -> int:
 
 
 def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None):
-    """Time `steps` full steps (quantize + attention).  Returns (ms/step, attention kernel ms)."""
+    """Time `steps` full steps (quantize + attention), then `steps` attention launches alone.
+    Returns (ms/step, attention kernel ms from the back-to-back launches, state)."""
     kv_tile = kv_tile or default_kv_tile(w.d)
     st = prepare_prefill(w, hf, torch)
     q4, k4, v4 = st["bufs"]
 
-    def step(timer=None):
+    def step():
         hf.quantize_qkv(st["q"], st["k"], st["v"], Hkv=w.Hkv, smooth=w.smooth, s=st["s"],
                         inv_s=st["inv"], out=st["bufs"])
-        ev = timer.start() if timer else None
         hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
                     causal=w.causal, smooth=w.smooth, reorder=reorder, out=st["out"],
                     kv_tile=kv_tile)
-        if timer:
-            timer.stop(ev)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    timer = Timer()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(timer)
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    return ms, timer.mean_ms(), st
+    # the attention kernel alone: `steps` back-to-back launches between two events on the
+    # launch stream (no per-launch event overhead inside the bracket)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
+                    causal=w.causal, smooth=w.smooth, reorder=reorder, out=st["out"],
+                    kv_tile=kv_tile)
+    e1.record()
+    torch.cuda.synchronize()
+    return ms, e0.elapsed_time(e1) / steps, st
 
 
 def run_decode(w, hf, torch, steps, warmup, copies=2):
@@ -142,25 +127,25 @@ def run_decode(w, hf, torch, steps, warmup, copies=2):
     nbytes = hf.hifa4_attn_workspace_bytes(w.B, w.Hq, 1, w.d, w.num_splits)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
-    def step(i, timer=None):
+    def step(i):
         k4, v4 = caches[i % copies]
-        ev = timer.start() if timer else None
         hf.attn_fwd(None, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=1, N_kv=w.N_kv, d=w.d,
                     causal=False, smooth=True, reorder=True, q_f16=q, s=s,
                     num_splits=w.num_splits, out=out, workspace=ws)
-        if timer:
-            timer.stop(ev)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    timer = Timer()
+    # back-to-back launches between two events on the launch stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        step(i, timer)
+        step(i)
+    e1.record()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    return ms, timer.mean_ms(), dict(q=q, s=s, caches=caches, out=out)
+    return ms, e0.elapsed_time(e1) / steps, dict(q=q, s=s, caches=caches, out=out)
 
 
 def sample_rows(w, n, seed=12345):

@@ -23,7 +23,7 @@
 //  * Prefill: a workgroup is 4 wavefronts that read the same KV head (the
 //    heads of one GQA group, or consecutive row blocks of one head); each
 //    K_hat/V_hat tile is loaded once per workgroup with 1 KB-contiguous
-//    direct global-to-LDS copies into a three-stage ring in MFMA operand order
+//    direct global-to-LDS copies into double-buffered stages in MFMA operand order
 //    (a lane reads its operand as one conflict-free 16-byte LDS load).  The
 //    grid's fastest dimension is the KV head, so the round-robin dispatch over
 //    the 8 XCDs keeps each KV head's tiles in one L2.
@@ -82,7 +82,9 @@ __device__ __forceinline__ int phat_exponent(float bmax, float c, float m_use) {
 // Four E2M1 code bytes (8 values, value i in nibble i) of S^T registers
 // r0..r0+7 of one block, RNE(x / sc).
 __device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
-  uint32_t w = cvt_fp4x2<0>(0u, x[r0], x[r0 + 1], sc);
+  // all four bytes are written: the initial word is a don't-care (a source
+  // register, which saves a move)
+  uint32_t w = cvt_fp4x2<0>(__float_as_uint(x[r0]), x[r0], x[r0 + 1], sc);
   w = cvt_fp4x2<1>(w, x[r0 + 2], x[r0 + 3], sc);
   w = cvt_fp4x2<2>(w, x[r0 + 4], x[r0 + 5], sc);
   return cvt_fp4x2<3>(w, x[r0 + 6], x[r0 + 7], sc);
@@ -319,8 +321,10 @@ struct Stage {
 // alike) and kb0 * D/32 to a scale source.
 template <int D, int KT>
 struct DmaPlan {
-  const uint8_t* src[Stage<D, KT>::CPW + 1];  // per lane; the last one is the scale unit
-  int dst[Stage<D, KT>::CPW + 1];             // LDS offset in the stage (wave-uniform)
+  // piece j: source base (wave-uniform) + per-lane 32-bit offset; the last one is the scale unit
+  const uint8_t* base[Stage<D, KT>::CPW + 1];
+  uint32_t off[Stage<D, KT>::CPW + 1];
+  int dst[Stage<D, KT>::CPW + 1];  // LDS offset in the stage (wave-uniform)
 };
 
 struct KvBases {
@@ -343,18 +347,22 @@ __device__ __forceinline__ void make_dma_plan(const KvBases& kv, DmaPlan<D, KT>&
     const int i = wave + 4 * j;
     if (i < S::N_KC) {
       const int b = i / S::KS, sk = i % S::KS;
-      pl.src[j] = kv.kc + (32 * b + l32) * (D / 2) + (2 * sk + hf) * 16;
+      pl.base[j] = kv.kc + 32 * b * (D / 2) + 2 * sk * 16;
+      pl.off[j] = (uint32_t)(l32 * (D / 2) + hf * 16);
       pl.dst[j] = S::KC_OFF + i * 1024;
     } else {
       const int jj = i - S::N_KC, u = jj / S::CT, ct = jj % S::CT;
-      pl.src[j] = kv.vc + (u * D + 32 * ct + l32) * 32 + 16 * hf;
+      pl.base[j] = kv.vc + (u * D + 32 * ct) * 32;
+      pl.off[j] = (uint32_t)(l32 * 32 + 16 * hf);
       pl.dst[j] = S::VC_OFF + jj * 1024;
     }
   }
-  constexpr int KU = S::KSC_BYTES / 16;
-  const int k = wave * (S::SCU / 4) + lane;  // scale unit of this lane (lanes < SCU/4)
-  pl.src[S::CPW] = k < KU ? kv.ks + k * 16 : kv.vs + (k - KU) * 16;
-  pl.dst[S::CPW] = S::KSC_OFF + wave * (S::SCU / 4) * 16;
+  // scale units: waves 0-1 copy K_hat's, waves 2-3 V_hat's (KSC_BYTES = VSC_BYTES)
+  constexpr int KU = S::KSC_BYTES / 16, PU = S::SCU / 4;
+  static_assert(KU == 2 * PU, "each wave's scale units come from one tensor");
+  pl.base[S::CPW] = wave < 2 ? kv.ks + wave * PU * 16 : kv.vs + (wave - 2) * PU * 16;
+  pl.off[S::CPW] = (uint32_t)(lane * 16);
+  pl.dst[S::CPW] = S::KSC_OFF + wave * PU * 16;
 }
 
 // Issue this wave's copies of the tile at kb0 into `stage`.  Completion is
@@ -365,11 +373,12 @@ __device__ __forceinline__ void dma_tile(const DmaPlan<D, KT>& pl, int kb0, uint
   using S = Stage<D, KT>;
 #pragma unroll
   for (int j = 0; j < S::CPW; j++)
-    __builtin_amdgcn_global_load_lds((const void*)(pl.src[j] + (int64_t)kb0 * (D / 2)),
+    __builtin_amdgcn_global_load_lds((const void*)(pl.base[j] + (int64_t)kb0 * (D / 2) + pl.off[j]),
                                      (lds_ptr_t)(stage + pl.dst[j]), 16, 0, 0);
   if ((threadIdx.x & 63) < S::SCU / 4)
-    __builtin_amdgcn_global_load_lds((const void*)(pl.src[S::CPW] + (int64_t)kb0 * (D / 32)),
-                                     (lds_ptr_t)(stage + pl.dst[S::CPW]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(pl.base[S::CPW] + (int64_t)kb0 * (D / 32) + pl.off[S::CPW]),
+        (lds_ptr_t)(stage + pl.dst[S::CPW]), 16, 0, 0);
 }
 
 // V_hat operands read from an LDS stage.
@@ -394,11 +403,10 @@ template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   using S = Stage<D, KT>;
   constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
-  // three stages as separate arrays, so that reads of one are not ordered
-  // behind the copies in flight into another
+  // two stages as separate arrays, so that reads of one are not ordered
+  // behind the copies in flight into the other
   __shared__ __attribute__((aligned(16))) uint8_t st0[S::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t st1[S::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[S::BYTES];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int nh = p.heads_per_wg, nr = 4 / nh;
@@ -454,52 +462,42 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     }
   }
 
-  // Pipeline over three LDS stages.  Iteration t: copy tile t+2 into the
-  // stage that held tile t-1 (free since the barrier that ended iteration
-  // t-1), run the softmax and PV of tile t (its S^T was computed at the end of
-  // iteration t-1), then issue the S^T MFMAs of tile t+1 -- they execute
-  // while the wave waits at the barrier that ends the iteration, which also
-  // waits for this wave's copies to land.
+  // Copy pipeline: tile t+1 is copied into the free stage right after the
+  // barrier that ended tile t-1 (the last reads of that stage), so the copy
+  // runs under tile t's compute; the barrier that ends tile t waits for it.
   DmaPlan<D, KT> plan;
   make_dma_plan<D, KT>(kv, plan);
   dma_tile<D, KT>(plan, 0, st0);
-  if (tiles > 1) dma_tile<D, KT>(plan, KT, st1);
   __syncthreads();
 
   v16f accO[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) accO[ct] = zero16();
   float m = kNegInf, l = 0.0f;
-  auto computes = [&](int t) { return wave_active && t < tiles && t * KT <= wave_last_key; };
-  v16f sacc[NB];
-  auto scores = [&](const uint8_t* st) {
-#pragma unroll
-    for (int bb = 0; bb < NB; bb++) {
-      uint4 ka[KS];
-#pragma unroll
-      for (int s = 0; s < KS; s++)
-        ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
-      uint32_t ksw[SW];
-      row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
-      sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
-    }
-  };
-  if (computes(0)) scores(st0);
-  auto step = [&](int t, const uint8_t* cur, const uint8_t* nxt, uint8_t* fill) {
+  auto step = [&](int t, const uint8_t* st, uint8_t* nxt) {
     const int kb0 = t * KT;
-    if (t + 2 < tiles) dma_tile<D, KT>(plan, kb0 + 2 * KT, fill);
-    if (computes(t)) {
+    if (t + 1 < tiles) dma_tile<D, KT>(plan, kb0 + KT, nxt);
+    if (wave_active && kb0 <= wave_last_key) {
+      v16f sacc[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; bb++) {
+        uint4 ka[KS];
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+          ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
+        uint32_t ksw[SW];
+        row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
+        sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
+      }
       const bool need_mask = (kb0 + KT - 1) > wave_lim;
-      LdsV<D, KT> vops{cur};
+      LdsV<D, KT> vops{st};
       softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
     }
-    if (computes(t + 1)) scores(nxt);
     __syncthreads();
   };
-  for (int t = 0; t < tiles; t += 3) {
-    step(t, st0, st1, st2);
-    if (t + 1 < tiles) step(t + 1, st1, st2, st0);
-    if (t + 2 < tiles) step(t + 2, st2, st0, st1);
+  for (int t = 0; t < tiles; t += 2) {
+    step(t, st0, st1);
+    if (t + 1 < tiles) step(t + 1, st1, st0);
   }
 
   if (wave_active && qrow < p.N_q) store_out<D>(p.out + (bh * p.N_q + qrow) * D, accO, l);

@@ -89,6 +89,51 @@ __device__ __forceinline__ void quant_row_block(const uint16_t* __restrict__ x, 
   scales[row * (d / 32) + blk] = sc;
 }
 
+// The same quantization with four lanes per 32-channel block (d = 64, 128,
+// 256): each lane loads 8 channels (16 bytes, so a wavefront reads 1 KB
+// contiguous per instruction), the block max is combined over the lane quad
+// with DPP, and each lane writes its 4 code bytes; lane 0 of the quad writes
+// the scale byte.  t4 = 4 * (block index) + lane-in-quad.
+template <int D>
+__device__ __forceinline__ void quant_row_quad(const uint16_t* __restrict__ x, const float* __restrict__ mult,
+                                               int64_t H, int64_t G, int64_t N, int64_t Npad, int64_t t4,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int64_t per_row = D / 32;
+  const int64_t block = t4 >> 2;
+  const int q = (int)(t4 & 3);
+  const int64_t row = block / per_row, blk = block % per_row;
+  const int64_t bh = row / Npad, n = row % Npad;
+  const bool live = n < N;  // the same for the whole quad
+  float v[8];
+  float amax = 0.0f;
+  if (live) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + (bh * N + n) * D + blk * 32 + q * 8);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = half_to_float((uint16_t)(raw[i] & 0xFFFFu));
+      v[2 * i + 1] = half_to_float((uint16_t)(raw[i] >> 16));
+    }
+    if (mult) {
+      const float4* mp = reinterpret_cast<const float4*>(mult + ((bh % H) / G) * D + blk * 32 + q * 8);
+      const float4 m0 = mp[0], m1 = mp[1];
+      v[0] = v[0] * m0.x; v[1] = v[1] * m0.y; v[2] = v[2] * m0.z; v[3] = v[3] * m0.w;
+      v[4] = v[4] * m1.x; v[5] = v[5] * m1.y; v[6] = v[6] * m1.z; v[7] = v[7] * m1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = quad_max(amax);
+  uint32_t out = 0u;
+  uint8_t sc = 0;
+  if (live) {
+    const int e = mx_exponent(amax);
+    out = pack8_fp4(v, pow2f(e));
+    sc = (uint8_t)(e + 127);
+  }
+  *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + blk * 16 + q * 4) = out;
+  if (q == 0) scales[row * (D / 32) + blk] = sc;
+}
+
 // Any d that is a multiple of 32 (the fused kernel below covers d = 64, 128, 256).
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mult, int64_t H, int64_t G,
@@ -150,8 +195,8 @@ __device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, int
 }
 
 // ---------------------------------------------------------------------------
-// Q, K and V of one call in a single launch (d = 64, 128, 256): blocks
-// [0, nq) quantize Q rows, [nq, nq + nk) K rows, the rest one V tile each.
+// Q, K and V of one call in a single launch (d = 64, 128, 256): the first
+// blocks quantize one V tile each, the following ones Q rows, then K rows.
 // One launch instead of three keeps the HBM stream going across the tensors.
 // ---------------------------------------------------------------------------
 struct QuantArgs {
@@ -161,7 +206,7 @@ struct QuantArgs {
   uint8_t* codes[2];
   uint8_t* scales[2];
   const uint16_t* v;
-  int64_t vN, vNpad;
+  int64_t vN, vNpad, vtiles;
   uint8_t* vcodes;
   uint8_t* vscales;
 };
@@ -170,18 +215,24 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile_lds[64 * (D + 8)];
   int64_t b = blockIdx.x;
+  // V tiles first: each is a load -> barrier -> transpose round trip, so they
+  // start while the streaming Q / K blocks keep HBM busy
+  if (b < a.vtiles) {
+    quant_v_tile<D>(a.v, a.vN, a.vNpad, b, tile_lds, a.vcodes, a.vscales);
+    return;
+  }
+  b -= a.vtiles;
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     if (b < a.blocks[i]) {
-      const int64_t t = b * 256 + threadIdx.x;
-      if (t < a.threads[i])
-        quant_row_block<D>(a.x[i], a.mult[i], a.H[i], a.G[i], a.N[i], a.Npad[i], t, a.codes[i],
-                           a.scales[i], D);
+      const int64_t t4 = b * 256 + threadIdx.x;
+      if (t4 < a.threads[i])
+        quant_row_quad<D>(a.x[i], a.mult[i], a.H[i], a.G[i], a.N[i], a.Npad[i], t4, a.codes[i],
+                          a.scales[i]);
       return;
     }
     b -= a.blocks[i];
   }
-  quant_v_tile<D>(a.v, a.vN, a.vNpad, b, tile_lds, a.vcodes, a.vscales);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,7 +286,7 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
     a.G[i] = Hs[i] / Hkv;
     a.N[i] = Ns[i];
     a.Npad[i] = pad_tokens(Ns[i]);
-    a.threads[i] = xs[i] ? B * Hs[i] * a.Npad[i] * (d / 32) : 0;
+    a.threads[i] = xs[i] ? 4 * B * Hs[i] * a.Npad[i] * (d / 32) : 0;  // 4 lanes per block
     a.blocks[i] = (a.threads[i] + 255) / 256;
     a.codes[i] = cs[i];
     a.scales[i] = ss[i];
@@ -245,8 +296,8 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
   a.vNpad = pad_tokens(N_kv);
   a.vcodes = v_codes;
   a.vscales = v_scales;
-  const int64_t vtiles = v ? B * Hkv * (a.vNpad / 64) : 0;
-  const int64_t blocks = a.blocks[0] + a.blocks[1] + vtiles;
+  a.vtiles = v ? B * Hkv * (a.vNpad / 64) : 0;
+  const int64_t blocks = a.blocks[0] + a.blocks[1] + a.vtiles;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
   switch (d) {
