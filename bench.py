@@ -11,7 +11,7 @@ Also reported (one JSON line, extra keys): the dominant kernel against the FP4
 MFMA roofline, the other prefill shapes, P-Reordering off, the split-KV decode
 step in GB/s against HBM, and the CPU oracle timed on a sample of rows.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu] [--decode-only]
 """
 from __future__ import annotations
 
@@ -302,6 +302,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="primary workload only (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the split-KV decode step (profiling runs); prints its own line")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference "
                          "for hardware byte counters)")
@@ -327,6 +329,18 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] reference copy of {a.copy_check} MiB done")
         del src, dst
+
+    if a.decode_only:
+        wd = synth.decode()
+        msd, attnd, _ = run_decode(wd, hf, torch, a.steps, a.warmup)
+        gbs = wd.kv_bytes / (attnd * 1e-3) / 1e9
+        log(f"[bench] decode: {attnd:.4f} ms, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
+        print(json.dumps({"metric": "decode KV GB/s", "value": round(gbs, 3), "unit": "GB/s",
+                          "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+                          "ms_per_step": round(msd, 5), "kernel_ms": round(attnd, 5),
+                          "config": {"workload": "decode B=64 Hq=32 Hkv=8 d=128 N_kv=8192 "
+                                                 "splits=16"}}), flush=True)
+        return
 
     # ---- primary: Qwen3-8B-shaped causal prefill, P-Reordering on
     w = synth.qwen3_8b()
