@@ -72,6 +72,16 @@ __device__ __forceinline__ v16f score_block(const uint4 (&ka)[D / 64], const uin
   return acc;
 }
 
+// PV MFMA of 64-key unit u: the V_hat scale of unit u is byte u of the scale word.
+__device__ __forceinline__ v16f pv_mfma(int u, const uint4& a, int sa, const uint4& b, int sb, v16f acc) {
+  switch (u) {
+    case 0: return mfma_fp4<0, 0>(a, sa, b, sb, acc);
+    case 1: return mfma_fp4<1, 0>(a, sa, b, sb, acc);
+    case 2: return mfma_fp4<2, 0>(a, sa, b, sb, acc);
+    default: return mfma_fp4<3, 0>(a, sa, b, sb, acc);
+  }
+}
+
 // Block exponent of P_hat from the block's largest valid score (bmax = -inf:
 // no valid key, -127): e = clamp(floor(fma(bmax, c, -m)) - 2, -127, 127).
 __device__ __forceinline__ int phat_exponent(float bmax, float c, float m_use) {
@@ -92,7 +102,7 @@ __device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
 
 // The online-softmax step of one tile of KT keys given its S^T blocks:
 // running max, P, P_hat, normalizer, O rescale and O^T += V_hat^T P_hat^T.
-// vops.a(u, ct) / vops.sc(ct) supply the V_hat operands (byte 2u of the scale
+// vops.a(u, ct) / vops.sc(ct) supply the V_hat operands (byte u of the scale
 // word is unit u's block).  lim: last valid key of this lane's query column.
 //
 // Lane (query q, half hf) holds, of every 32-key block, the 16 keys with bit 2
@@ -103,12 +113,22 @@ __device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
 // after which lane (q, hf) holds the full 32-code block 2u + hf of unit u --
 // the B operand of the PV product -- with its keys in the operand order
 // operand_key (the V_hat tiled layout stores tokens in the same order).
-template <int D, int KT, bool REORDER, bool DUMP, class VOps>
-__device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
-                                           float c, const VOps& vops, v16f (&accO)[D / 32],
-                                           float& m, float& l, uint8_t* phat_codes_row,
-                                           uint8_t* phat_scales_row) {
-  constexpr int CT = D / 32, NB = KT / 32, NU = KT / 64;
+// One tile's quantized probabilities, between the softmax and the PV product.
+template <int KT>
+struct TileP {
+  uint4 ph[KT / 64];  // P_hat codes: B operand of unit u (lane: block 2u + hf)
+  int psc[KT / 64];   // its E8M0 scale byte
+  float alpha;        // 2^(m_old - m_new) of this tile
+  float rsp;          // reorder = 0: this row's sum of P over the tile
+};
+
+// The softmax half of a tile: running max (m updated), alpha, P = 2^(S c - m),
+// the E2M1 codes of P_hat and, for reorder = 0, the row sum of P.
+template <int D, int KT, bool REORDER, bool DUMP>
+__device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
+                                              float c, float& m, TileP<KT>& tp,
+                                              uint8_t* phat_codes_row, uint8_t* phat_scales_row) {
+  constexpr int NB = KT / 32, NU = KT / 64;
   const int hf = (threadIdx.x >> 5) & 1;
 
   if (need_mask) {
@@ -155,7 +175,7 @@ __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool nee
 
   // per-block exponents; sc[bb]: the scale of block bb for this lane's elements
   float sc[NB];
-  int psc[NU];
+  int* psc = tp.psc;
 #pragma unroll
   for (int u = 0; u < NU; u++) {
     const int em = phat_exponent(mine[u], c, m_use);
@@ -174,7 +194,7 @@ __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool nee
 
   // P_hat codes: this lane's 16 keys of each block as two dwords, then one
   // swap per dword pair hands each lane the partner's half of its block
-  uint4 ph[NU];
+  uint4* ph = tp.ph;
 #pragma unroll
   for (int u = 0; u < NU; u++) {
     const uint32_t a0 = cvt8(s[2 * u], 0, sc[2 * u]), a1 = cvt8(s[2 * u], 8, sc[2 * u]);
@@ -193,14 +213,38 @@ __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool nee
     }
   }
 
-  // O <- alpha O (skipped when the max did not move for any column)
+  tp.alpha = alpha;
+  if constexpr (!REORDER) {
+    float rs = 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) rs = rs + s[bb][r];
+    tp.rsp = rs + other_half(rs);
+  }
+  m = m_new;
+}
+
+// O <- alpha O, skipped when the max did not move for any column.
+template <int D>
+__device__ __forceinline__ void rescale_o(v16f (&accO)[D / 32], float alpha) {
   if (!__all(alpha == 1.0f)) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ct++)
+    for (int ct = 0; ct < D / 32; ct++)
 #pragma unroll
       for (int r = 0; r < 16; r++) accO[ct][r] = accO[ct][r] * alpha;
   }
+}
 
+// The PV half of a tile (O already rescaled by the tile's alpha): the
+// normalizer l = fp16(fp32(alpha l) + rowsum) and O^T += V_hat^T P_hat^T.
+template <int D, int KT, bool REORDER, class VOps>
+__device__ __forceinline__ void pv_accumulate(const TileP<KT>& tp, const VOps& vops,
+                                              v16f (&accO)[D / 32], float& l) {
+  constexpr int CT = D / 32, NU = KT / 64;
+  const uint4* ph = tp.ph;
+  const int* psc = tp.psc;
+  const float alpha = tp.alpha;
   // normalizer: l = fp16(fp32(alpha l) + rowsum)
   float rs;
   if constexpr (REORDER) {
@@ -212,12 +256,7 @@ __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool nee
     for (int u = 1; u < NU; u++) sl = mfma_fp4<0, 0>(ones, 127, ph[u], psc[u], sl);
     rs = sl[0];
   } else {
-    rs = 0.0f;
-#pragma unroll
-    for (int bb = 0; bb < NB; bb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) rs = rs + s[bb][r];
-    rs = rs + other_half(rs);
+    rs = tp.rsp;
   }
   const float al = alpha * l;
   l = round_f16(al + rs);
@@ -227,14 +266,20 @@ __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool nee
   for (int ct = 0; ct < CT; ct++) {
     const int vsc = (int)vops.sc(ct);
 #pragma unroll
-    for (int u = 0; u < NU; u++) {
-      if (u == 0)
-        accO[ct] = mfma_fp4<0, 0>(vops.a(0, ct), vsc, ph[0], psc[0], accO[ct]);
-      else
-        accO[ct] = mfma_fp4<2, 0>(vops.a(u, ct), vsc, ph[u], psc[u], accO[ct]);
-    }
+    for (int u = 0; u < NU; u++) accO[ct] = pv_mfma(u, vops.a(u, ct), vsc, ph[u], psc[u], accO[ct]);
   }
-  m = m_new;
+}
+
+// A whole tile: softmax, rescale, normalizer and PV, in that order.
+template <int D, int KT, bool REORDER, bool DUMP, class VOps>
+__device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
+                                           float c, const VOps& vops, v16f (&accO)[D / 32],
+                                           float& m, float& l, uint8_t* phat_codes_row,
+                                           uint8_t* phat_scales_row) {
+  TileP<KT> tp;
+  softmax_quant<D, KT, REORDER, DUMP>(s, kb0, need_mask, lim, c, m, tp, phat_codes_row, phat_scales_row);
+  rescale_o<D>(accO, tp.alpha);
+  pv_accumulate<D, KT, REORDER>(tp, vops, accO, l);
 }
 
 // o / l from the hardware reciprocal and one residual correction (Markstein):
@@ -392,9 +437,10 @@ struct LdsV {
   __device__ __forceinline__ uint32_t sc(int ct) const {
     const int lane = threadIdx.x & 63, hf = lane >> 5, ch = 32 * ct + (lane & 31);
     const uint8_t* p = st + Stage<D, KT>::VSC_OFF + ch * 2;
-    uint32_t w = ((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) >> (8 * hf)) & 0xFFu;
-    if constexpr (KT == 128)
-      w |= (((uint32_t)(*reinterpret_cast<const uint16_t*>(p + D * 2)) >> (8 * hf)) & 0xFFu) << 16;
+    uint32_t w = 0u;
+#pragma unroll
+    for (int u = 0; u < KT / 64; u++)
+      w |= (((uint32_t)(*reinterpret_cast<const uint16_t*>(p + u * D * 2)) >> (8 * hf)) & 0xFFu) << (8 * u);
     return w;
   }
 };
@@ -547,7 +593,7 @@ __device__ __forceinline__ void reg_load_v(const KvBases& kv, int kb0, RegOps<D,
       const int64_t tile = kb0 / 64 + u;
       op.va[u][ct] = *reinterpret_cast<const uint4*>(kv.vc + (tile * D + ch) * 32 + 16 * hf);
       const uint32_t sb = (uint32_t)(*reinterpret_cast<const uint16_t*>(kv.vs + (tile * D + ch) * 2)) >> (8 * hf);
-      w |= (sb & 0xFFu) << (16 * u);
+      w |= (sb & 0xFFu) << (8 * u);
     }
     op.vsw[ct] = w;
   }
