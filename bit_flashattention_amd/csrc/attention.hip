@@ -132,16 +132,14 @@ __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool 
   const int hf = (threadIdx.x >> 5) & 1;
 
   if (need_mask) {
-    // key offset o within the tile is valid when o <= room; the select is done
-    // with a sign mask and a bitfield insert so that it needs no scalar masks
+    // key offset o within the tile is valid when o <= room
     const int room = lim - kb0 - 4 * hf;
 #pragma unroll
     for (int bb = 0; bb < NB; bb++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int o = 32 * bb + 8 * (r / 4) + (r % 4);
-        const uint32_t drop = (uint32_t)((room - o) >> 31);  // all ones when o > room
-        s[bb][r] = __uint_as_float((drop & 0xFF800000u) | (~drop & __float_as_uint(s[bb][r])));
+        s[bb][r] = (room < o) ? kNegInf : s[bb][r];
       }
   }
 
@@ -437,11 +435,14 @@ struct LdsV {
   __device__ __forceinline__ uint32_t sc(int ct) const {
     const int lane = threadIdx.x & 63, hf = lane >> 5, ch = 32 * ct + (lane & 31);
     const uint8_t* p = st + Stage<D, KT>::VSC_OFF + ch * 2;
-    uint32_t w = 0u;
-#pragma unroll
-    for (int u = 0; u < KT / 64; u++)
-      w |= (((uint32_t)(*reinterpret_cast<const uint16_t*>(p + u * D * 2)) >> (8 * hf)) & 0xFFu) << (8 * u);
-    return w;
+    const uint32_t x0 = *reinterpret_cast<const uint16_t*>(p);
+    if constexpr (KT == 64) {
+      return x0 >> (8 * hf);
+    } else {
+      // byte 0 <- byte hf of unit 0's pair, byte 1 <- byte hf of unit 1's pair
+      const uint32_t x1 = *reinterpret_cast<const uint16_t*>(p + D * 2);
+      return __builtin_amdgcn_perm(x1, x0, 0x0C0C0400u + 0x0101u * (uint32_t)hf);
+    }
   }
 };
 
