@@ -92,6 +92,8 @@ def _load():
         lib.orc_f32_from_f16_array.argtypes = [vp, i64, vp]
         lib.orc_score.argtypes = [vp, vp, vp, vp, i64]
         lib.orc_score.restype = ctypes.c_float
+        lib.orc_rope_f16.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, i64, vp]
+        lib.orc_rope_f16.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -193,6 +195,21 @@ def quantize_v(v: np.ndarray):
     scales = np.zeros((B, H, d, Np // 32), dtype=np.uint8)
     _load().orc_quantize_v(_p(_f16bits(v)), B, H, N, Np, d, _p(codes), _p(scales))
     return codes, scales
+
+
+def rope_f16(x: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray, pos0: int = 0) -> np.ndarray:
+    """Rotate-half RoPE of binary16 rows [B][H][N][d] at positions pos0.. with fp32 tables
+    [n_rope][d/2]; binary16 result (one fp32 rounding per product and per sum)."""
+    B, H, N, d = x.shape
+    c = np.ascontiguousarray(cos_t, dtype=np.float32)
+    s = np.ascontiguousarray(sin_t, dtype=np.float32)
+    assert c.shape == s.shape and c.shape[1] == d // 2
+    out = np.zeros((B, H, N, d), dtype=np.uint16)
+    rc = _load().orc_rope_f16(_p(_f16bits(x)), B, H, N, d, pos0, _p(c), _p(s), c.shape[0],
+                              _p(out))
+    if rc != 0:
+        raise ValueError("orc_rope_f16: bad sizes")
+    return out.view(np.float16)
 
 
 def attn(B, Hq, Hkv, N_q, N_kv, d, *, causal, reorder, kv_tile=64, num_splits=1,

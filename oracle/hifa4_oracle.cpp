@@ -275,6 +275,34 @@ void orc_quantize_v(const uint16_t* v, int64_t B, int64_t H, int64_t N, int64_t 
       }
 }
 
+// RoPE of binary16 rows before Smooth-QK (the abstract places Smooth-QK after
+// RoPE).  The pages do not define RoPE; the reading is the rotate-half form:
+// channel j < d/2 pairs with j + d/2 and the pair turns by the angle whose
+// cosine and sine the caller tabulates per absolute position p = pos0 + n:
+//   r[j]       = fp32(x[j] * cos) - fp32(x[j + d/2] * sin)
+//   r[j + d/2] = fp32(x[j + d/2] * cos) + fp32(x[j] * sin)
+// each product and sum one fp32 rounding, and r stored as binary16 (the
+// binary16 post-RoPE K that the row quantizer takes).
+int orc_rope_f16(const uint16_t* x, int64_t B, int64_t H, int64_t N, int64_t d, int64_t pos0,
+                 const float* cos_t, const float* sin_t, int64_t n_rope, uint16_t* out) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || d % 2 != 0 || pos0 < 0 || pos0 + N > n_rope)
+    return -1;
+  const int64_t half = d / 2;
+  for (int64_t r = 0; r < B * H * N; r++) {
+    const int64_t p = pos0 + r % N;
+    const uint16_t* xr = x + r * d;
+    uint16_t* o = out + r * d;
+    for (int64_t j = 0; j < half; j++) {
+      const float c = cos_t[p * half + j], s = sin_t[p * half + j];
+      const float a = f16_to_f32(xr[j]), b = f16_to_f32(xr[j + half]);
+      const float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+      o[j] = f16_rne(ac - bs);
+      o[j + half] = f16_rne(bc + as);
+    }
+  }
+  return 0;
+}
+
 int64_t orc_inexact_count(void) { return g_inexact.load(); }
 void orc_reset_inexact(void) { g_inexact.store(0); }
 

@@ -70,6 +70,15 @@ void orc_quantize_rows(const uint16_t* x, int64_t B, int64_t H, int64_t Hkv, int
 void orc_quantize_v(const uint16_t* v, int64_t B, int64_t H, int64_t N, int64_t Npad, int64_t d,
                     uint8_t* codes, uint8_t* scales);
 
+/* RoPE (rotate-half: channel j < d/2 pairs with j + d/2) of binary16 rows
+ * x [B][H][N][d] at positions pos0 .. pos0+N-1, tables cos/sin [n_rope][d/2]
+ * fp32 (row = absolute position):
+ *   out[j]       = f16(fp32(x[j] cos) - fp32(x[j+d/2] sin))
+ *   out[j + d/2] = f16(fp32(x[j+d/2] cos) + fp32(x[j] sin))
+ * Returns 0, or -1 for bad sizes (odd d, pos0 + N > n_rope). */
+int orc_rope_f16(const uint16_t* x, int64_t B, int64_t H, int64_t N, int64_t d, int64_t pos0,
+                 const float* cos_t, const float* sin_t, int64_t n_rope, uint16_t* out);
+
 typedef struct {
   int64_t B, Hq, Hkv, N_q, N_kv, d;
   int64_t Npad_q, Npad_kv;  /* row counts of the padded Q and K/V layouts */

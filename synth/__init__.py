@@ -19,6 +19,8 @@ Workloads (sizes from the benchmark configurations; every tensor is BHSD):
                     4 K outlier channels x4 per KV head.
 * ``decode``        B=64, Hq=32, Hkv=8, d=128, one query per sequence, KV length
                     8192 built with the ``qwen3_8b`` recipe.
+* ``kv_append``     the decode cache's shape (B=64, Hkv=8, d=128, 8192 tokens) with K
+                    drawn before RoPE, plus RoPE tables (theta 1e6), for cache appends.
 
 Each workload accepts shape overrides so that tests can build scaled-down
 instances with the same structure.
@@ -227,6 +229,51 @@ def decode(B=64, Hq=32, Hkv=8, N_kv=8192, d=128, num_splits=16, kv_tile=64,
     v = tensor(seed_of(wid, TAG_V), B, Hkv, N_kv, d)
     w = Workload("decode", B, Hq, Hkv, 1, N_kv, d, False, True, 0.5, kv_tile, num_splits, (1,),
                  q, k, v)
+    w.q_cal = tensor(seed_of(wid, TAG_QCAL), 1, Hq, n_cal, d, 1e6)
+    w.k_cal = tensor(seed_of(wid, TAG_KCAL), 1, Hkv, n_cal, d, 1e6, mult, off)
+    return w
+
+
+def rope_table(theta: float, d: int, n_pos: int, pos0: int = 0):
+    """RoPE cosine and sine tables [n_pos][d/2] fp32 for positions pos0 .. pos0+n_pos-1:
+    angle (pos0 + p) * theta^(-2j/d), evaluated in double and rounded once to fp32 (the
+    same angles ``tensor`` rotates by)."""
+    j = np.arange(d // 2, dtype=np.float64)
+    inv_freq = np.power(float(theta), -2.0 * j / float(d))
+    ang = (pos0 + np.arange(n_pos, dtype=np.float64))[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@dataclass
+class AppendWorkload:
+    """A decode-time KV-cache append problem: binary16 K (before RoPE) and V of N tokens per
+    (sequence, KV head), RoPE tables for positions 0..N-1, Smooth-QK calibration tensors.
+    A test or benchmark appends tokens [pos, pos + T) of these tensors to a 4-bit cache."""
+    name: str
+    B: int
+    Hkv: int
+    Hq: int
+    N: int
+    d: int
+    theta: float
+    alpha: float
+    k_raw: np.ndarray = field(repr=False, default=None)
+    v: np.ndarray = field(repr=False, default=None)
+    cos: np.ndarray = field(repr=False, default=None)
+    sin: np.ndarray = field(repr=False, default=None)
+    q_cal: Optional[np.ndarray] = field(repr=False, default=None)
+    k_cal: Optional[np.ndarray] = field(repr=False, default=None)
+
+
+def kv_append(B=64, Hkv=8, Hq=32, N=8192, d=128, n_cal=512) -> AppendWorkload:
+    """Decode-shaped cache (B=64, Hkv=8, d=128, RoPE theta 1e6, the decode workload's 8 x12
+    outlier channels and offsets), here drawn before RoPE: the append applies RoPE itself."""
+    wid = 6
+    mult, off = _head_structure(wid, Hkv, d, 8, 12.0, 2.0)
+    k_raw = tensor(seed_of(wid, TAG_K), B, Hkv, N, d, 0.0, mult, off)
+    v = tensor(seed_of(wid, TAG_V), B, Hkv, N, d)
+    cos, sin = rope_table(1e6, d, N)
+    w = AppendWorkload("kv_append", B, Hkv, Hq, N, d, 1e6, 0.5, k_raw, v, cos, sin)
     w.q_cal = tensor(seed_of(wid, TAG_QCAL), 1, Hq, n_cal, d, 1e6)
     w.k_cal = tensor(seed_of(wid, TAG_KCAL), 1, Hkv, n_cal, d, 1e6, mult, off)
     return w
