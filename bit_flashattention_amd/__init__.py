@@ -43,13 +43,14 @@ class AttnArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("kv_tile", ctypes.c_int), ("num_splits", ctypes.c_int),
         ("phat_codes", ctypes.c_void_p), ("phat_scales", ctypes.c_void_p),
+        ("kv_capacity", ctypes.c_int64),
     ]
 
 
 EXPORTS = (
     "hifa4_version", "hifa4_status_str", "hifa4_last_error", "hifa4_mx4_bytes",
     "hifa4_calibrate_smooth", "hifa4_quantize_qkv", "hifa4_attn_workspace_bytes",
-    "hifa4_attn_fwd",
+    "hifa4_attn_fwd", "hifa4_kv_append",
 )
 
 
@@ -78,6 +79,9 @@ def load(path: str = LIB_PATH):
     lib.hifa4_attn_fwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci,
                                    ctypes.POINTER(AttnArgs), vp]
     lib.hifa4_attn_fwd.restype = ci
+    lib.hifa4_kv_append.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, ci, vp,
+                                    vp, vp, vp, vp, vp, vp]
+    lib.hifa4_kv_append.restype = ci
     _lib = lib
     return lib
 
@@ -125,6 +129,13 @@ def hifa4_quantize_qkv(q, k, v, B, Hq, Hkv, N_q, N_kv, d, smooth, s, inv_s, q_co
 def hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args: AttnArgs, stream):
     _check(load().hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, int(causal), int(smooth), int(reorder),
                                  ctypes.byref(args), stream), "hifa4_attn_fwd")
+
+
+def hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos, rope_sin, rope_rows,
+                    smooth, inv_s, k_codes, k_scales, v_codes, v_scales, v_stage, stream):
+    _check(load().hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos,
+                                  rope_sin, rope_rows, int(smooth), inv_s, k_codes, k_scales,
+                                  v_codes, v_scales, v_stage, stream), "hifa4_kv_append")
 
 
 # ---------------------------------------------------------------------------
@@ -195,7 +206,8 @@ def quantize_qkv(q=None, k=None, v=None, *, Hkv: int, smooth: bool = False, s=No
 
 
 def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, workspace=None,
-              num_splits: int = 1, kv_tile: int = 64, phat: Optional[MX4] = None) -> AttnArgs:
+              num_splits: int = 1, kv_tile: int = 64, phat: Optional[MX4] = None,
+              kv_capacity: int = 0) -> AttnArgs:
     a = AttnArgs()
     a.q_codes = _ptr(q4.codes) if q4 else None
     a.q_scales = _ptr(q4.scales) if q4 else None
@@ -210,14 +222,16 @@ def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, w
     a.num_splits = num_splits
     a.phat_codes = _ptr(phat.codes) if phat else None
     a.phat_scales = _ptr(phat.scales) if phat else None
+    a.kv_capacity = kv_capacity
     return a
 
 
 def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, N_q: int,
              N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool, q_f16=None, s=None,
              num_splits: int = 1, kv_tile: int = 64, out=None, workspace=None,
-             phat: Optional[MX4] = None, stream=None):
-    """4-bit attention forward; returns out [B][Hq][N_q][d] binary16."""
+             phat: Optional[MX4] = None, kv_capacity: int = 0, stream=None):
+    """4-bit attention forward; returns out [B][Hq][N_q][d] binary16.  kv_capacity: token
+    rows of the K/V buffers when they are a cache larger than N_kv (0: padded N_kv)."""
     import torch
     dev = k4.codes.device
     if out is None:
@@ -226,6 +240,41 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
         nbytes = hifa4_attn_workspace_bytes(B, Hq, N_q, d, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=workspace,
-                     num_splits=num_splits, kv_tile=kv_tile, phat=phat)
+                     num_splits=num_splits, kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity)
     hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args, _stream(stream))
     return out
+
+
+@dataclass
+class KVCache:
+    """A 4-bit KV cache of `capacity` token rows per (sequence, KV head): K in the row layout,
+    V in the tiled token layout, and the binary16 staging rows of the V block still filling."""
+    k4: MX4
+    v4: MX4
+    v_stage: "object"
+    capacity: int
+
+
+def empty_kv_cache(B: int, Hkv: int, capacity: int, d: int, device="cuda") -> KVCache:
+    """Zeroed cache (positions never appended read as zero codes with scale byte 0)."""
+    import torch
+    if capacity % TOKEN_PAD:
+        raise ValueError(f"capacity must be a multiple of {TOKEN_PAD}")
+    k4 = empty_mx4(False, B, Hkv, capacity, d, device)
+    v4 = empty_mx4(True, B, Hkv, capacity, d, device)
+    for t in (k4.codes, k4.scales, v4.codes, v4.scales):
+        t.zero_()
+    stage = torch.zeros((B, Hkv, 32, d), dtype=torch.float16, device=device)
+    return KVCache(k4, v4, stage, capacity)
+
+
+def kv_append(cache: KVCache, k_new=None, v_new=None, *, pos: int, rope_cos=None, rope_sin=None,
+              smooth: bool = False, inv_s=None, stream=None) -> None:
+    """Append tokens [pos, pos + T) ([B][Hkv][T][d] binary16; K before RoPE) to the cache."""
+    ref = k_new if k_new is not None else v_new
+    B, Hkv, T, d = ref.shape
+    rows = 0 if rope_cos is None else rope_cos.shape[0]
+    hifa4_kv_append(_ptr(k_new), _ptr(v_new), B, Hkv, T, d, pos, cache.capacity, _ptr(rope_cos),
+                    _ptr(rope_sin), rows, smooth, _ptr(inv_s), _ptr(cache.k4.codes),
+                    _ptr(cache.k4.scales), _ptr(cache.v4.codes), _ptr(cache.v4.scales),
+                    _ptr(cache.v_stage), _stream(stream))

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libhifa4.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "quantize.hip", "attention.hip"]
+SOURCES = ["api.hip", "quantize.hip", "attention.hip", "kv_append.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every multiply and add the kernels write stays a separate IEEE

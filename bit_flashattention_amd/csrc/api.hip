@@ -64,7 +64,7 @@ bool supported_d(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
 extern "C" {
 
-int hifa4_version(void) { return 100; }
+int hifa4_version(void) { return 101; }
 
 const char* hifa4_status_str(hifa4_status s) {
   switch (s) {
@@ -213,6 +213,10 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
       (a->q_f16 && !aligned(a->q_f16, 16)) || (a->s && !aligned(a->s, 16)) || !aligned(a->out_f16, 8) ||
       (a->phat_codes && !aligned(a->phat_codes, 16)) || (a->workspace && !aligned(a->workspace, 16)))
     return fail(HIFA4_EINVAL, "attn: misaligned buffer");
+  const int64_t cap = a->kv_capacity ? a->kv_capacity : hifa4::pad_tokens(N_kv);
+  if (cap < N_kv || cap % hifa4::kTokenPad != 0)
+    return fail(HIFA4_EINVAL, "attn: kv_capacity must be a multiple of %d and >= N_kv",
+                (int)hifa4::kTokenPad);
   size_t need = 0;
   hifa4_attn_workspace_bytes(B, Hq, N_q, d, a->num_splits, &need);
   hifa4_status st = check_device();
@@ -248,7 +252,7 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   L.N_kv = N_kv;
   L.d = d;
   L.Npad_q = hifa4::pad_tokens(N_q);
-  L.Npad_kv = hifa4::pad_tokens(N_kv);
+  L.Npad_kv = cap;
   L.causal = causal ? 1 : 0;
   L.smooth = smooth ? 1 : 0;
   L.reorder = reorder ? 1 : 0;
@@ -261,6 +265,51 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
     e = hifa4::launch_attn_prefill(L, (hipStream_t)stream);
   }
   if (e != hipSuccess) return hip_fail(e, "attn launch");
+  return ok();
+}
+
+hifa4_status hifa4_kv_append(const void* k_new_f16, const void* v_new_f16, int64_t B,
+                             int64_t Hkv, int64_t T, int64_t d, int64_t pos,
+                             int64_t kv_capacity, const float* rope_cos, const float* rope_sin,
+                             int64_t rope_rows, int smooth, const float* inv_s,
+                             uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                             uint8_t* v_scales, void* v_stage_f16, void* stream) {
+  if (B < 0 || Hkv <= 0 || T < 0 || pos < 0)
+    return fail(HIFA4_EINVAL, "kv_append: need B, T, pos >= 0 and Hkv > 0");
+  if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "kv_append: d must be a positive multiple of 32");
+  if (!supported_d(d)) return fail(HIFA4_EUNSUPPORTED, "kv_append: d = %lld not built (64, 128, 256)", (long long)d);
+  if (kv_capacity <= 0 || kv_capacity % hifa4::kTokenPad != 0 || pos + T > kv_capacity)
+    return fail(HIFA4_EINVAL, "kv_append: kv_capacity must be a positive multiple of %d with pos + T <= kv_capacity",
+                (int)hifa4::kTokenPad);
+  if ((rope_cos != nullptr) != (rope_sin != nullptr))
+    return fail(HIFA4_EINVAL, "kv_append: rope_cos and rope_sin go together");
+  if (k_new_f16 && rope_cos && rope_rows < pos + T)
+    return fail(HIFA4_EINVAL, "kv_append: the RoPE tables need at least pos + T rows");
+  if (k_new_f16 && smooth && !inv_s) return fail(HIFA4_EINVAL, "kv_append: smooth = 1 needs inv_s");
+  if ((k_new_f16 && (!k_codes || !k_scales)) || (v_new_f16 && (!v_codes || !v_scales || !v_stage_f16)))
+    return fail(HIFA4_EINVAL, "kv_append: missing cache or staging buffer");
+  const float* cs = k_new_f16 ? rope_cos : nullptr;
+  const float* sn = k_new_f16 ? rope_sin : nullptr;
+  const float* is = (k_new_f16 && smooth) ? inv_s : nullptr;
+  const void* a16[] = {k_new_f16, v_new_f16, cs, sn, is, k_new_f16 ? k_codes : nullptr,
+                       v_new_f16 ? v_codes : nullptr, v_new_f16 ? v_stage_f16 : nullptr};
+  for (const void* p : a16)
+    if (p && !aligned(p, 16)) return fail(HIFA4_EINVAL, "kv_append: misaligned buffer");
+  if (B == 0 || T == 0 || (!k_new_f16 && !v_new_f16)) return ok();
+  hifa4_status st = check_device();
+  if (st) return st;
+  const void* ptrs[] = {k_new_f16, v_new_f16, cs, sn, is,
+                        k_new_f16 ? k_codes : nullptr, k_new_f16 ? k_scales : nullptr,
+                        v_new_f16 ? v_codes : nullptr, v_new_f16 ? v_scales : nullptr,
+                        v_new_f16 ? v_stage_f16 : nullptr};
+  const char* names[] = {"k_new", "v_new", "rope_cos", "rope_sin", "inv_s", "k_codes",
+                         "k_scales", "v_codes", "v_scales", "v_stage"};
+  for (int i = 0; i < 10; i++)
+    if ((st = check_dev_ptr(ptrs[i], names[i]))) return st;
+  hipError_t e = hifa4::launch_kv_append(k_new_f16, v_new_f16, B, Hkv, T, d, pos, kv_capacity,
+                                         cs, sn, is, k_codes, k_scales, v_codes, v_scales,
+                                         v_new_f16 ? v_stage_f16 : nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return ok();
 }
 

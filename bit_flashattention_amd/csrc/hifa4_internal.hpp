@@ -24,6 +24,12 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
                             uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
                             uint8_t* v_scales, hipStream_t stream);
 
+hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t T,
+                            int64_t d, int64_t pos, int64_t cap, const float* cos_t,
+                            const float* sin_t, const float* inv_s, uint8_t* k_codes,
+                            uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales, void* stage,
+                            hipStream_t stream);
+
 // Everything one attention launch needs (device pointers + sizes).
 struct AttnLaunch {
   const uint8_t* q_codes;

@@ -150,6 +150,11 @@ typedef struct {
    * tiles a row never visits are left as the caller initialized them. */
   uint8_t* phat_codes;
   uint8_t* phat_scales;
+  /* Token rows of the K/V layouts (a multiple of HIFA4_TOKEN_PAD, >= N_kv),
+   * for a cache allocated larger than N_kv (hifa4_kv_append); 0 means
+   * N_kv rounded up to HIFA4_TOKEN_PAD.  The P_hat dump rows use the same
+   * count: [..][kv_capacity/2] and [..][kv_capacity/32]. */
+  int64_t kv_capacity;
 } hifa4_attn_args;
 
 /* Workspace bytes hifa4_attn_fwd needs for these sizes (0 when num_splits = 1). */
@@ -177,6 +182,46 @@ hifa4_status hifa4_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t N_q, int6
 hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
                             int64_t d, int causal, int smooth, int reorder,
                             const hifa4_attn_args* args, void* stream);
+
+/*
+ * Decode-time KV-cache append (HiFA4 Abstract: Smooth-QK rescales K after
+ * RoPE; both GEMMs take 4-bit operands).  Appends the T new tokens of every
+ * (sequence, KV head) at positions pos .. pos+T-1 of a 4-bit cache with
+ * kv_capacity token rows (a multiple of HIFA4_TOKEN_PAD, pos + T <=
+ * kv_capacity), so that afterwards the cache holds, for positions
+ * 0 .. pos+T-1, exactly what hifa4_quantize_qkv writes for the whole
+ * post-RoPE sequence (row layout K, tiled token layout V):
+ *   K: k_new_f16 [B][Hkv][T][d] binary16 before RoPE.  With tables
+ *      (rope_cos, rope_sin [rope_rows][d/2] fp32, row = absolute position,
+ *      rope_rows >= pos + T) each row is rotated rotate-half style, channel
+ *      j < d/2 paired with j + d/2:
+ *        r[j]       = fp32(k[j] cos) - fp32(k[j + d/2] sin)
+ *        r[j + d/2] = fp32(k[j + d/2] cos) + fp32(k[j] sin)
+ *      and rounded to binary16 (NULL tables: r = k, already rotated).  Then
+ *      x = fp32(r * inv_s[g][j]) (smooth = 1) or r, and one MX block per 32
+ *      channels into K rows pos .. pos+T-1.
+ *   V: v_new_f16 [B][Hkv][T][d].  Every 32-position block that the new tokens
+ *      touch is quantized again from the binary16 values of all its tokens so
+ *      far (positions after pos+T-1 count as 0).  The values of the block
+ *      still filling are kept in v_stage_f16 [B][Hkv][32][d] binary16 (slot =
+ *      position % 32), which the caller allocates and must not modify
+ *      between appends.  Only this call fills it, and its contents matter
+ *      for the positions of that block before pos: appends either start at
+ *      a multiple of 32 (a fresh cache, pos = 0, needs no initialization)
+ *      or continue a cache that earlier appends built.
+ * Either k_new_f16 or v_new_f16 may be NULL to skip that tensor (its cache
+ * pointers are then ignored).  Cache rows and blocks outside the touched
+ * range are left untouched: a cache the decode step reads must hold zero
+ * codes and scale bytes there (allocate it zeroed).  d in {64, 128, 256}.
+ * Appends on one cache must be issued in position order on one stream.
+ * Asynchronous.
+ */
+hifa4_status hifa4_kv_append(const void* k_new_f16, const void* v_new_f16, int64_t B,
+                             int64_t Hkv, int64_t T, int64_t d, int64_t pos,
+                             int64_t kv_capacity, const float* rope_cos, const float* rope_sin,
+                             int64_t rope_rows, int smooth, const float* inv_s,
+                             uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
+                             uint8_t* v_scales, void* v_stage_f16, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(hf):
 
 def test_status_strings_and_version(hf):
     lib = hf.load()
-    assert lib.hifa4_version() == 100
+    assert lib.hifa4_version() == 101
     for s in range(6):
         assert lib.hifa4_status_str(s)
     assert b"unknown" in lib.hifa4_status_str(99)
@@ -87,6 +87,8 @@ def _args(hf, **kw):
     (dict(args=dict(phat_codes=0x1000)), "EINVAL"),      # codes without scales
     (dict(args=dict(num_splits=4), N_q=16), "EUNSUPPORTED"),  # 16 rows x 4 heads > 32
     (dict(args=dict(k_codes=0x1008)), "EINVAL"),         # misaligned
+    (dict(args=dict(kv_capacity=200)), "EINVAL"),        # not a multiple of 128
+    (dict(args=dict(kv_capacity=128)), "EINVAL"),        # below N_kv = 256
 ])
 def test_attn_validation(hf, case, status):
     shape = dict(B=1, Hq=8, Hkv=2, N_q=64, N_kv=256, d=128, causal=0)
@@ -162,3 +164,45 @@ def test_product_path_does_not_reference_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "hifa4_oracle" not in txt, f
+
+
+def _append(hf, **kw):
+    """hifa4_kv_append with plausible (never dereferenced) pointers, overridden by kw."""
+    p = 0x10000
+    a = dict(k=p, v=p, B=2, Hkv=2, T=3, d=128, pos=61, cap=256, cos=p, sin=p, rows=64, smooth=1,
+             inv_s=p, kc=p, ks=p, vc=p, vs=p, stage=p)
+    a.update(kw)
+    hf.hifa4_kv_append(a["k"], a["v"], a["B"], a["Hkv"], a["T"], a["d"], a["pos"], a["cap"],
+                       a["cos"], a["sin"], a["rows"], a["smooth"], a["inv_s"], a["kc"], a["ks"],
+                       a["vc"], a["vs"], a["stage"], None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(Hkv=0), "EINVAL"),
+    (dict(T=-1), "EINVAL"),
+    (dict(d=100), "EINVAL"),
+    (dict(d=96), "EUNSUPPORTED"),
+    (dict(cap=200), "EINVAL"),                  # not a multiple of 128
+    (dict(pos=250, T=7), "EINVAL"),             # past the capacity
+    (dict(sin=None), "EINVAL"),                 # cos without sin
+    (dict(rows=63), "EINVAL"),                  # table shorter than pos + T
+    (dict(inv_s=None), "EINVAL"),               # smooth without inv_s
+    (dict(kc=None), "EINVAL"),
+    (dict(stage=None), "EINVAL"),
+    (dict(vc=0x10008), "EINVAL"),               # misaligned
+])
+def test_kv_append_validation(hf, case, status):
+    with pytest.raises(hf.HiFA4Error) as e:
+        _append(hf, **case)
+    assert e.value.status == getattr(hf, status)
+    assert hf.load().hifa4_last_error()
+
+
+def test_kv_append_empty_is_noop(hf):
+    _append(hf, T=0)
+    _append(hf, B=0)
+    _append(hf, k=None, v=None)
+    # skipped tensors need none of their buffers
+    with pytest.raises(hf.HiFA4Error) as e:
+        _append(hf, v=None, vc=None, vs=None, stage=None)
+    assert e.value.status in (hf.ENODEV, hf.EINVAL)  # valid sizes: fails only at the device check
