@@ -148,6 +148,52 @@ def run_decode(w, hf, torch, steps, warmup, copies=2):
     return ms, e0.elapsed_time(e1) / steps, dict(q=q, s=s, caches=caches, out=out)
 
 
+def append_bytes(w, T, pos):
+    """Algorithmic HBM bytes of one append of T tokens at `pos` (every (b, g)): read the new K
+    and V rows and the staged V of the first touched block, the RoPE table rows and inv_s; write
+    the K_hat rows, every touched V_hat block (d codes of 16 B + d scale bytes) and the staging
+    rows of a block left filling."""
+    d, bg = w.d, w.B * w.Hkv
+    blocks = (pos + T - 1) // 32 - pos // 32 + 1
+    staged_in = pos % 32
+    staged_out = (pos + T) % 32 if (pos + T) // 32 > pos // 32 else ((pos + T) % 32 - pos % 32
+                                                                     if (pos + T) % 32 else 0)
+    per_bg = (2 * T * d * 2 + staged_in * d * 2 + T * (d // 2 + d // 32) + blocks * d * 17
+              + staged_out * d * 2)
+    return bg * per_bg + T * d * 4 + w.Hkv * d * 4
+
+
+def run_append(w, hf, torch, steps, warmup, T):
+    """Decode-time KV append: a cache of N-1 tokens built by one append (untimed), then `steps`
+    back-to-back appends of the tokens [N-T, N) at position N-T (each rewrites the same rows and
+    blocks, so every launch does the same work) between two events."""
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    s, inv = hf.calibrate_smooth(up(w.q_cal), up(w.k_cal), w.alpha)
+    cos, sin = up(w.cos), up(w.sin)
+    cache = hf.empty_kv_cache(w.B, w.Hkv, hf.padded(w.N + 1), w.d)
+    k_all, v_all = up(w.k_raw), up(w.v)
+    pos = w.N - T
+    hf.kv_append(cache, k_all[:, :, :pos].contiguous(), v_all[:, :, :pos].contiguous(), pos=0,
+                 rope_cos=cos, rope_sin=sin, smooth=True, inv_s=inv)
+    kn, vn = k_all[:, :, pos:].contiguous(), v_all[:, :, pos:].contiguous()
+    del k_all, v_all
+
+    def step():
+        hf.kv_append(cache, kn, vn, pos=pos, rope_cos=cos, rope_sin=sin, smooth=True, inv_s=inv)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return ms, append_bytes(w, T, pos)
+
+
 def sample_rows(w, n, seed=12345):
     rng = np.random.default_rng(seed)
     total = w.B * w.Hq * w.N_q
@@ -304,6 +350,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decode step (profiling runs); prints its own line")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only the KV-cache appends (profiling runs); prints its own line")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference "
                          "for hardware byte counters)")
@@ -340,6 +388,20 @@ def main():
                           "ms_per_step": round(msd, 5), "kernel_ms": round(attnd, 5),
                           "config": {"workload": "decode B=64 Hq=32 Hkv=8 d=128 N_kv=8192 "
                                                  "splits=16"}}), flush=True)
+        return
+
+    if a.append_only:
+        wa = synth.kv_append()
+        lines = {}
+        for T in (1, 128):
+            ms, nb = run_append(wa, hf, torch, a.steps, a.warmup, T)
+            lines[f"T{T}"] = {"us": round(ms * 1e3, 3), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
+            log(f"[bench] kv_append T={T}: {ms * 1e3:.2f} us, {nb / ms / 1e6:.1f} GB/s")
+        print(json.dumps({"metric": "KV append us", "value": lines["T1"]["us"], "unit": "us",
+                          "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+                          "higher_is_better": False, "appends": lines,
+                          "config": {"workload": "kv_append B=64 Hkv=8 d=128 cache 8192 tokens"}}),
+              flush=True)
         return
 
     # ---- primary: Qwen3-8B-shaped causal prefill, P-Reordering on
@@ -410,6 +472,18 @@ def main():
                            "kv_gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
         log(f"[bench] decode: {attnd:.4f} ms, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
         del std
+        torch.cuda.empty_cache()
+        wa = synth.kv_append()
+        extra["kv_append"] = {"workload": "kv_append B=64 Hkv=8 d=128: RoPE + Smooth-QK + MXFP4 of "
+                                          "the new K rows, V blocks re-quantized, cache of 8192 "
+                                          "tokens"}
+        for T in (1, 128):
+            msa, nba = run_append(wa, hf, torch, a.steps, a.warmup, T)
+            extra["kv_append"][f"T{T}"] = {"us": msa * 1e3, "alg_bytes": nba,
+                                           "gbs": nba / msa / 1e6,
+                                           "frac_hbm_peak": nba / msa / 1e6 / HBM_PEAK_GBS}
+            log(f"[bench] kv_append T={T}: {msa * 1e3:.2f} us ({nba / msa / 1e6:.1f} GB/s)")
+        del wa
         torch.cuda.empty_cache()
     if not a.no_cpu:
         cl = cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0)

@@ -14,12 +14,15 @@
 //      that adds to it; those values wait in a caller-owned staging buffer
 //      [B][Hkv][32][d] until the block is full.
 //
-// Work split (grid = B*Hkv x chunks, 256 threads): the items are K blocks (one
-// token row x 32 channels) and V blocks (one channel x 32 positions).  Only
-// chunk 0 of a (b, g) reads the staging buffer (the first touched V block, whose
-// older tokens sit there) and only chunk 0 writes it, after a barrier, so no
-// other workgroup ever touches it.  HBM-bound; a one-token append is a few
-// hundred bytes per (b, g) and is bounded by launch latency.
+// Work split (grid = B*Hkv x (K chunks + V chunks), 256 threads): K block
+// pairs (one token row x the 32 channels of a block and of its RoPE partner,
+// one thread each) are dealt over the K chunks;
+// V is handled per 64-position tile, staged through LDS by a whole V-chunk
+// workgroup.  Only V chunk 0 of a (b, g) reads the staging buffer (in the first
+// touched tile, which holds the positions before the call) and only it writes
+// the buffer, after that tile's last barrier, so no other workgroup touches
+// it.  HBM-bound in bulk; a one-token append moves about 10 KB per (b, g) and
+// is bounded by latency.
 #include "hifa4_device.hpp"
 #include "hifa4_internal.hpp"
 
@@ -37,8 +40,8 @@ struct AppendArgs {
   uint8_t* v_scales;      //                    [B][Hkv][cap/64][d][2]
   uint16_t* stage;        // [B][Hkv][32][d] binary16
   int64_t Hkv, T, pos, cap;
-  int64_t n_k, n_v;       // K items (T * d/32) and V items after the first block
-  int chunks;
+  int64_t n_k;            // K items: T * d/64 pairs of 32-channel blocks
+  int chunks_k, chunks_v; // workgroups per (b, g) for K and for V
 };
 
 __device__ __forceinline__ void load32_f16(const uint16_t* p, float (&x)[32]) {
@@ -78,95 +81,131 @@ __device__ __forceinline__ void mx32(const float (&x)[32], u32x4& codes, uint8_t
   scale = (uint8_t)(e + 127);
 }
 
-// K: token t of the call, channels [32 blk, 32 blk + 32).
+// K: token t of the call, the channel blocks [32 pb, 32 pb + 32) and its RoPE
+// partner [32 pb + d/2, 32 pb + d/2 + 32): both rows of each rotated pair come
+// from one load of each half and one table row.
+__device__ __forceinline__ void store_k_block(const AppendArgs& a, int64_t row, int blk, int D,
+                                              const float (&x)[32]) {
+  u32x4 codes;
+  uint8_t sc;
+  mx32(x, codes, sc);
+  *reinterpret_cast<u32x4*>(a.k_codes + row * (D / 2) + 16 * blk) = codes;
+  a.k_scales[row * (D / 32) + blk] = sc;
+}
+
 template <int D>
-__device__ void append_k_block(const AppendArgs& a, int64_t bg, int64_t t, int blk) {
+__device__ void append_k_pair(const AppendArgs& a, int64_t bg, int64_t t, int pb) {
   constexpr int HALF = D / 2;
   const int64_t p = a.pos + t;
-  const uint16_t* row = a.k + (bg * a.T + t) * D;
-  const int j0 = 32 * blk;
-  const bool lo = j0 < HALF;
-  float x[32];
-  load32_f16(row + j0, x);
+  const uint16_t* src = a.k + (bg * a.T + t) * D;
+  const int j0 = 32 * pb;
+  float lo[32], hi[32];
+  load32_f16(src + j0, lo);
+  load32_f16(src + j0 + HALF, hi);
   if (a.cos_t) {
-    // rotate-half: r[j] = x[j] c - x[j + d/2] s (j < d/2), r[j] = x[j] c + x[j - d/2] s
-    // (j >= d/2), each product and the sum one fp32 rounding, r kept as binary16
-    const int jj = lo ? j0 : j0 - HALF;
-    float y[32], c[32], s[32];
-    load32_f16(row + (lo ? j0 + HALF : j0 - HALF), y);
-    load32_f32(a.cos_t + p * HALF + jj, c);
-    load32_f32(a.sin_t + p * HALF + jj, s);
+    // rotate-half: r[j] = x[j] c - x[j + d/2] s, r[j + d/2] = x[j + d/2] c + x[j] s,
+    // each product and each sum one fp32 rounding, r kept as binary16
+    float c[32], s[32];
+    load32_f32(a.cos_t + p * HALF + j0, c);
+    load32_f32(a.sin_t + p * HALF + j0, s);
 #pragma unroll
     for (int i = 0; i < 32; i++) {
-      const float xc = x[i] * c[i], ys = y[i] * s[i];
-      x[i] = half_to_float(float_to_half_bits(lo ? xc - ys : xc + ys));
+      const float ac = lo[i] * c[i], bs = hi[i] * s[i], bc = hi[i] * c[i], as = lo[i] * s[i];
+      lo[i] = half_to_float(float_to_half_bits(ac - bs));
+      hi[i] = half_to_float(float_to_half_bits(bc + as));
     }
   }
   if (a.inv_s) {
-    float m[32];
-    load32_f32(a.inv_s + (bg % a.Hkv) * D + j0, m);
+    const float* m = a.inv_s + (bg % a.Hkv) * D + j0;
+    float ml[32], mh[32];
+    load32_f32(m, ml);
+    load32_f32(m + HALF, mh);
 #pragma unroll
-    for (int i = 0; i < 32; i++) x[i] = x[i] * m[i];
+    for (int i = 0; i < 32; i++) {
+      lo[i] = lo[i] * ml[i];
+      hi[i] = hi[i] * mh[i];
+    }
   }
-  u32x4 codes;
-  uint8_t sc;
-  mx32(x, codes, sc);
-  *reinterpret_cast<u32x4*>(a.k_codes + (bg * a.cap + p) * (D / 2) + 16 * blk) = codes;
-  a.k_scales[(bg * a.cap + p) * (D / 32) + blk] = sc;
+  const int64_t row = bg * a.cap + p;
+  store_k_block(a, row, pb, D, lo);
+  store_k_block(a, row, pb + HALF / 32, D, hi);
 }
 
-// V: channel ch of the 32-position block beta, from the staging buffer (positions
-// before the call), the new tokens, and zeros after them; written in the tiled
-// token layout with nibble k holding position 32 beta + operand_key(k).
+// V: the touched 32-position blocks of 64-position tile tau.  The workgroup
+// stages their binary16 rows in LDS (16-byte loads from the staging buffer for
+// positions before the call, from the new tokens, zeros after them), then each
+// thread quantizes one (block, channel) column, with nibble k holding position
+// 32 beta + operand_key(k), into the tiled token layout.  Ends with a barrier,
+// so the LDS tile may be reused and every read of the staging buffer is done.
 template <int D>
-__device__ void append_v_block(const AppendArgs& a, int64_t bg, int64_t beta, int ch) {
+__device__ void append_v_tile(const AppendArgs& a, int64_t bg, int64_t tau, uint16_t* lds) {
+  constexpr int ROW = D + 8;  // padded LDS row (binary16): column reads spread over banks
+  const int tid = threadIdx.x;
   const int64_t end = a.pos + a.T;
-  float x[32];
-#pragma unroll
-  for (int k = 0; k < 32; k++) {
-    const int64_t n = 32 * beta + operand_key(k);
-    uint16_t h = 0;
+  const int64_t b_first = a.pos / 32, b_last = (end - 1) / 32;
+  const int64_t blo = 2 * tau > b_first ? 2 * tau : b_first;
+  const int64_t bhi = 2 * tau + 1 < b_last ? 2 * tau + 1 : b_last;
+  const int nblk = (int)(bhi - blo + 1);
+  const int r0 = (int)(32 * blo - 64 * tau);
+  for (int i = tid; i < 32 * nblk * (D / 8); i += 256) {
+    const int r = r0 + i / (D / 8), c8 = i % (D / 8);
+    const int64_t n = 64 * tau + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
     if (n < a.pos)
-      h = a.stage[(bg * 32 + (n & 31)) * D + ch];
+      val = *reinterpret_cast<const u32x4*>(a.stage + (bg * 32 + (n & 31)) * D + c8 * 8);
     else if (n < end)
-      h = a.v[(bg * a.T + (n - a.pos)) * D + ch];
-    x[k] = half_to_float(h);
+      val = *reinterpret_cast<const u32x4*>(a.v + (bg * a.T + (n - a.pos)) * D + c8 * 8);
+    *reinterpret_cast<u32x4*>(&lds[r * ROW + c8 * 8]) = val;
   }
-  u32x4 codes;
-  uint8_t sc;
-  mx32(x, codes, sc);
-  const int64_t tile = bg * (a.cap / 64) + beta / 2;
-  *reinterpret_cast<u32x4*>(a.v_codes + (tile * D + ch) * 32 + 16 * (beta & 1)) = codes;
-  a.v_scales[(tile * D + ch) * 2 + (beta & 1)] = sc;
+  __syncthreads();
+  const int64_t tile = bg * (a.cap / 64) + tau;
+  for (int i = tid; i < nblk * D; i += 256) {
+    const int64_t beta = blo + i / D;
+    const int ch = i % D, rb = (int)(32 * beta - 64 * tau);
+    float x[32];
+#pragma unroll
+    for (int k = 0; k < 32; k++) x[k] = half_to_float(lds[(rb + operand_key(k)) * ROW + ch]);
+    u32x4 codes;
+    uint8_t sc;
+    mx32(x, codes, sc);
+    *reinterpret_cast<u32x4*>(a.v_codes + (tile * D + ch) * 32 + 16 * (beta & 1)) = codes;
+    a.v_scales[(tile * D + ch) * 2 + (beta & 1)] = sc;
+  }
+  __syncthreads();
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[64 * (D + 8)];
   const int64_t bg = blockIdx.x;
-  const int chunk = blockIdx.y, tid = threadIdx.x;
-  const int64_t beta0 = a.pos / 32;
-  // K blocks and the V blocks after the first one, dealt over all chunks
-  const int64_t stride = 256LL * a.chunks;
-  for (int64_t i = (int64_t)chunk * 256 + tid; i < a.n_k + a.n_v; i += stride) {
-    if (i < a.n_k)
-      append_k_block<D>(a, bg, i / (D / 32), (int)(i % (D / 32)));
-    else
-      append_v_block<D>(a, bg, beta0 + 1 + (i - a.n_k) / D, (int)((i - a.n_k) % D));
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.y < a.chunks_k) {
+    // K blocks, dealt over the K chunks
+    const int64_t stride = 256LL * a.chunks_k;
+    for (int64_t i = (int64_t)blockIdx.y * 256 + tid; i < a.n_k; i += stride)
+      append_k_pair<D>(a, bg, i / (D / 64), (int)(i % (D / 64)));
+    return;
   }
-  if (chunk != 0 || !a.v) return;
-  // the first touched V block (its older positions come from the staging buffer)
-  for (int ch = tid; ch < D; ch += 256) append_v_block<D>(a, bg, beta0, ch);
-  __syncthreads();  // every read of the staging buffer is done
-  // keep the new tokens of the block that is still filling
+  // V tiles, dealt over the V chunks
+  const int chunk = (int)blockIdx.y - a.chunks_k;
   const int64_t end = a.pos + a.T;
-  if (end % 32 == 0) return;
-  const int64_t first = end / 32 * 32 > a.pos ? end / 32 * 32 : a.pos;
-  const int64_t cnt = end - first;
-  for (int64_t i = tid; i < cnt * D; i += 256) {
-    const int64_t n = first + i / D;
-    const int ch = (int)(i % D);
-    a.stage[(bg * 32 + (n & 31)) * D + ch] = a.v[(bg * a.T + (n - a.pos)) * D + ch];
+  const int64_t tau0 = a.pos / 64, tau1 = (end - 1) / 64;
+  if (chunk == 0) {
+    // the first touched tile: its older positions come from the staging buffer
+    append_v_tile<D>(a, bg, tau0, lds);
+    // every read of the staging buffer is done: keep the new tokens of the
+    // block that is still filling
+    if (end % 32 != 0) {
+      const int64_t first = end / 32 * 32 > a.pos ? end / 32 * 32 : a.pos;
+      for (int64_t i = tid; i < (end - first) * (D / 8); i += 256) {
+        const int64_t n = first + i / (D / 8);
+        const int c8 = (int)(i % (D / 8));
+        *reinterpret_cast<u32x4*>(a.stage + (bg * 32 + (n & 31)) * D + c8 * 8) =
+            *reinterpret_cast<const u32x4*>(a.v + (bg * a.T + (n - a.pos)) * D + c8 * 8);
+      }
+    }
   }
+  for (int64_t tau = tau0 + 1 + chunk; tau <= tau1; tau += a.chunks_v) append_v_tile<D>(a, bg, tau, lds);
 }
 
 hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t T,
@@ -190,14 +229,15 @@ hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv
   a.T = T;
   a.pos = pos;
   a.cap = cap;
-  a.n_k = k ? T * (d / 32) : 0;
-  a.n_v = v ? ((pos + T - 1) / 32 - pos / 32) * d : 0;
-  // about four items per thread, at most 128 chunks per (b, g)
-  const int64_t per_chunk = 4 * 256;
-  int64_t chunks = (a.n_k + a.n_v + per_chunk - 1) / per_chunk;
-  chunks = chunks < 1 ? 1 : (chunks > 128 ? 128 : chunks);
-  a.chunks = (int)chunks;
-  const dim3 grid((unsigned)(B * Hkv), (unsigned)chunks), block(256);
+  a.n_k = k ? T * (d / 64) : 0;
+  // separate workgroups for K (one block per thread) and V (one 64-position
+  // tile each), so a short append's two round trips overlap; at most 128 of
+  // each per (b, g)
+  const int64_t tiles = v ? (pos + T - 1) / 64 - pos / 64 + 1 : 0;
+  const int64_t ck = (a.n_k + 255) / 256;
+  a.chunks_k = (int)(ck > 128 ? 128 : ck);
+  a.chunks_v = (int)(tiles > 128 ? 128 : tiles);
+  const dim3 grid((unsigned)(B * Hkv), (unsigned)(a.chunks_k + a.chunks_v)), block(256);
   switch (d) {
     case 64: kv_append_kernel<64><<<grid, block, 0, stream>>>(a); break;
     case 128: kv_append_kernel<128><<<grid, block, 0, stream>>>(a); break;
