@@ -184,6 +184,7 @@ def run_append(w, hf, torch, steps, warmup, T):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    ref = [t.clone() for t in (cache.k4.codes, cache.k4.scales, cache.v4.codes, cache.v4.scales)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -191,7 +192,34 @@ def run_append(w, hf, torch, steps, warmup, T):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    return ms, append_bytes(w, T, pos)
+    # the same appends replayed from a captured graph: GPU time without the per-call host
+    # cost (argument checks, ctypes), checked against the eager cache after every replay
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps):
+                    step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / steps)
+            got = (cache.k4.codes, cache.k4.scales, cache.v4.codes, cache.v4.scales)
+            if not all(torch.equal(a, b) for a, b in zip(got, ref)):
+                raise RuntimeError("graph replay changed the cache")
+        graph_ms = min(times)
+        del g
+    except RuntimeError as e:
+        log(f"[bench] kv_append graph timing skipped: {e}")
+    return ms, append_bytes(w, T, pos), graph_ms
 
 
 def sample_rows(w, n, seed=12345):
@@ -394,9 +422,12 @@ def main():
         wa = synth.kv_append()
         lines = {}
         for T in (1, 128):
-            ms, nb = run_append(wa, hf, torch, a.steps, a.warmup, T)
-            lines[f"T{T}"] = {"us": round(ms * 1e3, 3), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
-            log(f"[bench] kv_append T={T}: {ms * 1e3:.2f} us, {nb / ms / 1e6:.1f} GB/s")
+            ms, nb, gms = run_append(wa, hf, torch, a.steps, a.warmup, T)
+            lines[f"T{T}"] = {"us": round(ms * 1e3, 3), "bytes": nb, "gbs": round(nb / ms / 1e6, 1),
+                              "graph_us": None if gms is None else round(gms * 1e3, 3)}
+            log(f"[bench] kv_append T={T}: {ms * 1e3:.2f} us per call ({nb / ms / 1e6:.1f} GB/s)"
+                + ("" if gms is None else f"; from a graph {gms * 1e3:.2f} us "
+                                          f"({nb / gms / 1e6:.1f} GB/s)"))
         print(json.dumps({"metric": "KV append us", "value": lines["T1"]["us"], "unit": "us",
                           "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
                           "higher_is_better": False, "appends": lines,
@@ -478,11 +509,15 @@ def main():
                                           "the new K rows, V blocks re-quantized, cache of 8192 "
                                           "tokens"}
         for T in (1, 128):
-            msa, nba = run_append(wa, hf, torch, a.steps, a.warmup, T)
-            extra["kv_append"][f"T{T}"] = {"us": msa * 1e3, "alg_bytes": nba,
-                                           "gbs": nba / msa / 1e6,
-                                           "frac_hbm_peak": nba / msa / 1e6 / HBM_PEAK_GBS}
-            log(f"[bench] kv_append T={T}: {msa * 1e3:.2f} us ({nba / msa / 1e6:.1f} GB/s)")
+            msa, nba, gma = run_append(wa, hf, torch, a.steps, a.warmup, T)
+            best = msa if gma is None else min(msa, gma)
+            extra["kv_append"][f"T{T}"] = {"us_per_call": msa * 1e3, "alg_bytes": nba,
+                                           "us_graph": None if gma is None else gma * 1e3,
+                                           "gbs": nba / best / 1e6,
+                                           "frac_hbm_peak": nba / best / 1e6 / HBM_PEAK_GBS}
+            log(f"[bench] kv_append T={T}: {msa * 1e3:.2f} us per call"
+                + ("" if gma is None else f", {gma * 1e3:.2f} us from a graph")
+                + f" ({nba / best / 1e6:.1f} GB/s)")
         del wa
         torch.cuda.empty_cache()
     if not a.no_cpu:

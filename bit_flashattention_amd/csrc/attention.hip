@@ -557,6 +557,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
 // read pre-quantized).  Each chunk writes its (m, l, O) partial state.
 // ---------------------------------------------------------------------------
 
+// A 16-byte load with the nontemporal hint: the split-KV path reads each KV
+// cache byte once per step, so its stream should not displace cached lines
+// (measured: 5% faster on the B=64, 8192-token decode).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // K_hat / V_hat operands of one tile held in registers (split-KV path).
 template <int D, int KT>
 struct RegOps {
@@ -577,7 +585,7 @@ __device__ __forceinline__ void reg_load_k(const KvBases& kv, int kb0, RegOps<D,
     const int64_t key = kb0 + 32 * bb + l32;
     const uint8_t* kr = kv.kc + key * (D / 2);
 #pragma unroll
-    for (int s = 0; s < D / 64; s++) op.ka[bb][s] = *reinterpret_cast<const uint4*>(kr + (2 * s + hf) * 16);
+    for (int s = 0; s < D / 64; s++) op.ka[bb][s] = load_stream16(kr + (2 * s + hf) * 16);
     row_scales<D>(kv.ks + key * (D / 32), hf, op.ksw[bb]);
   }
 }
@@ -592,7 +600,7 @@ __device__ __forceinline__ void reg_load_v(const KvBases& kv, int kb0, RegOps<D,
 #pragma unroll
     for (int u = 0; u < KT / 64; u++) {
       const int64_t tile = kb0 / 64 + u;
-      op.va[u][ct] = *reinterpret_cast<const uint4*>(kv.vc + (tile * D + ch) * 32 + 16 * hf);
+      op.va[u][ct] = load_stream16(kv.vc + (tile * D + ch) * 32 + 16 * hf);
       const uint32_t sb = (uint32_t)(*reinterpret_cast<const uint16_t*>(kv.vs + (tile * D + ch) * 2)) >> (8 * hf);
       w |= (sb & 0xFFu) << (8 * u);
     }
