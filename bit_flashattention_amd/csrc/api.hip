@@ -204,9 +204,11 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   if ((a->phat_codes != nullptr) != (a->phat_scales != nullptr))
     return fail(HIFA4_EINVAL, "attn: phat codes and scales go together");
   const int64_t G = Hq / Hkv;
-  const bool split_path = a->num_splits > 1 || a->q_f16 != nullptr;
-  if (split_path && G * N_q > hifa4::kRowsPerWave)
-    return fail(HIFA4_EUNSUPPORTED, "attn: split-KV / raw-Q path needs N_q * Hq/Hkv <= 32");
+  if (a->num_splits > 1 && G * N_q > hifa4::kRowsPerWave)
+    return fail(HIFA4_EUNSUPPORTED, "attn: split-KV needs N_q * Hq/Hkv <= 32");
+  // decode-shaped calls (a few query rows per KV head) take the split-KV kernels,
+  // the rest the prefill kernel; both quantize a raw binary16 Q themselves
+  const bool split_path = a->num_splits > 1 || (a->q_f16 != nullptr && G * N_q <= hifa4::kRowsPerWave);
   if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 16) ||
       !aligned(a->v_scales, 16) ||
       (a->q_codes && (!aligned(a->q_codes, 16) || !aligned(a->q_scales, 8))) ||

@@ -306,6 +306,55 @@ __device__ __forceinline__ void store_out(uint16_t* orow, const v16f (&accO)[D /
     }
 }
 
+// Smooth-QK multiply and MX quantization of one query row inside the kernel,
+// exactly as the quantize pass does it (x = fp32(q * s[j]), one block per 32
+// channels): the lane of half hf builds the B operand of k-step s from
+// channels 64 s + 32 hf .. + 32, one whole block, so no lane exchange is
+// needed.  qx = NULL gives a zero row (padding columns).
+template <int D>
+__device__ __forceinline__ void quantize_query_lane(const uint16_t* qx, const float* srow,
+                                                    uint4 (&qb)[D / 64], uint32_t (&qsc)[(D / 64 + 1) / 2]) {
+  constexpr int KS = D / 64, SW = (D / 64 + 1) / 2;
+  const int hf = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int w = 0; w < SW; w++) qsc[w] = 0u;
+#pragma unroll
+  for (int s = 0; s < KS; s++) {
+    const int cb = 2 * s + hf;
+    float v[32];
+    if (qx) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(qx + cb * 32 + 8 * u);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int z = 0; z < 4; z++) {
+          v[8 * u + 2 * z] = half_to_float((uint16_t)(w[z] & 0xFFFFu));
+          v[8 * u + 2 * z + 1] = half_to_float((uint16_t)(w[z] >> 16));
+        }
+      }
+      if (srow) {
+        const float* sp = srow + cb * 32;
+#pragma unroll
+        for (int z = 0; z < 32; z++) v[z] = v[z] * sp[z];
+      }
+    } else {
+#pragma unroll
+      for (int z = 0; z < 32; z++) v[z] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int z = 0; z < 32; z++) amax = fmaxf(amax, fabsf(v[z]));
+    const int e = mx_exponent(amax);
+    const float sc = pow2f(e);
+    qb[s].x = pack8_fp4(&v[0], sc);
+    qb[s].y = pack8_fp4(&v[8], sc);
+    qb[s].z = pack8_fp4(&v[16], sc);
+    qb[s].w = pack8_fp4(&v[24], sc);
+    qsc[s / 2] |= (uint32_t)(qx ? e + 127 : 0) << (16 * (s % 2));
+  }
+}
+
 struct KParams {
   const uint8_t* q_codes;
   const uint8_t* q_scales;
@@ -485,10 +534,22 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   const int64_t qrow = row0 + l32;
   const int lim = CAUSAL ? (int)min64(qrow + shift, p.N_kv - 1) : (int)(p.N_kv - 1);
 
+  // Copy pipeline: tile t+1 is copied into the free stage right after the
+  // barrier that ended tile t-1 (the last reads of that stage), so the copy
+  // runs under tile t's compute; the barrier that ends tile t waits for it.
+  // The first tile's copy is issued before the query work so that it overlaps.
+  DmaPlan<D, KT> plan;
+  make_dma_plan<D, KT>(kv, plan);
+  dma_tile<D, KT>(plan, 0, st0);
+
   // Q_hat rows of this wave: B operand of S^T, resident for the whole loop.
   uint4 qb[KS];
   uint32_t qsc[SW];
-  if (wave_active) {
+  if (wave_active && p.q_f16) {
+    // raw binary16 query: Smooth-QK and quantization here (rows past N_q are zero)
+    quantize_query_lane<D>(qrow < p.N_q ? p.q_f16 + (bh * p.N_q + qrow) * D : nullptr,
+                           p.s ? p.s + g * D : nullptr, qb, qsc);
+  } else if (wave_active) {
     const uint8_t* qr = p.q_codes + (bh * p.Npad_q + qrow) * (D / 2);
 #pragma unroll
     for (int s = 0; s < KS; s++) qb[s] = *reinterpret_cast<const uint4*>(qr + (2 * s + hf) * 16);
@@ -509,12 +570,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     }
   }
 
-  // Copy pipeline: tile t+1 is copied into the free stage right after the
-  // barrier that ended tile t-1 (the last reads of that stage), so the copy
-  // runs under tile t's compute; the barrier that ends tile t waits for it.
-  DmaPlan<D, KT> plan;
-  make_dma_plan<D, KT>(kv, plan);
-  dma_tile<D, KT>(plan, 0, st0);
   __syncthreads();
 
   v16f accO[CT];
@@ -641,43 +696,7 @@ __device__ __forceinline__ void split_query(const KParams& p, int64_t b, int64_t
 #pragma unroll
   for (int w = 0; w < SW; w++) qsc[w] = 0u;
   if constexpr (QRAW) {
-    // Smooth-QK multiply and MX quantization of 32 channels per k-step, in-lane.
-    const uint16_t* qx = p.q_f16 + row * D;
-#pragma unroll
-    for (int s = 0; s < KS; s++) {
-      const int cb = 2 * s + hf;
-      float v[32];
-      if (real) {
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(qx + cb * 32 + 8 * u);
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int z = 0; z < 4; z++) {
-            v[8 * u + 2 * z] = half_to_float((uint16_t)(w[z] & 0xFFFFu));
-            v[8 * u + 2 * z + 1] = half_to_float((uint16_t)(w[z] >> 16));
-          }
-        }
-        if (p.s) {
-          const float* sp = p.s + g * D + cb * 32;
-#pragma unroll
-          for (int z = 0; z < 32; z++) v[z] = v[z] * sp[z];
-        }
-      } else {
-#pragma unroll
-        for (int z = 0; z < 32; z++) v[z] = 0.0f;
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int z = 0; z < 32; z++) amax = fmaxf(amax, fabsf(v[z]));
-      const int e = mx_exponent(amax);
-      const float sc = pow2f(e);
-      qb[s].x = pack8_fp4(&v[0], sc);
-      qb[s].y = pack8_fp4(&v[8], sc);
-      qb[s].z = pack8_fp4(&v[16], sc);
-      qb[s].w = pack8_fp4(&v[24], sc);
-      qsc[s / 2] |= (uint32_t)(real ? e + 127 : 0) << (16 * (s % 2));
-    }
+    quantize_query_lane<D>(real ? p.q_f16 + row * D : nullptr, p.s ? p.s + g * D : nullptr, qb, qsc);
   } else {
     const int64_t qr_idx = (b * p.Hq + h) * p.Npad_q + i;
     const uint8_t* qr = p.q_codes + qr_idx * (D / 2);

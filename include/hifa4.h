@@ -125,7 +125,8 @@ typedef struct {
   const uint8_t* q_codes;
   const uint8_t* q_scales;
   /* ... or raw binary16 [B][Hq][N_q][d], smoothed with `s` (when smooth = 1)
-   * and quantized inside the kernel exactly as hifa4_quantize_qkv would. */
+   * and quantized inside the kernel exactly as hifa4_quantize_qkv would
+   * (any N_q with num_splits = 1; N_q * Hq/Hkv <= 32 with num_splits > 1). */
   const void* q_f16;
   const float* s;
   /* K row layout, V tiled token layout (from hifa4_quantize_qkv). */

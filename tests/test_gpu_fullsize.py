@@ -51,14 +51,16 @@ def check_quantized(got, ref, v_layout=False):
     assert np.array_equal(scales.reshape(-1), rs.reshape(-1))
 
 
-@pytest.mark.parametrize("name,reorder", [("qwen3_8b", 1), ("qwen3_8b", 0), ("gemma2_9b", 1),
-                                          ("llama_batched", 1), ("llama_batched", 0)])
-def test_prefill_full_size(hf, name, reorder):
+@pytest.mark.parametrize("name,reorder,raw_q", [("qwen3_8b", 1, True), ("qwen3_8b", 1, False),
+                                                ("qwen3_8b", 0, True), ("gemma2_9b", 1, True),
+                                                ("llama_batched", 1, True),
+                                                ("llama_batched", 0, False)])
+def test_prefill_full_size(hf, name, reorder, raw_q):
     import torch
     w = synth.WORKLOADS[name]()
     kt = bench_kv_tile(w.d)
     print(f"[fullsize] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N_q} d={w.d} reorder={reorder} "
-          f"kv_tile={kt}", flush=True)
+          f"kv_tile={kt} raw_q={raw_q}", flush=True)
     if w.smooth:
         s, inv = hf.calibrate_smooth(to_dev(w.q_cal), to_dev(w.k_cal), w.alpha)
         s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
@@ -67,8 +69,12 @@ def test_prefill_full_size(hf, name, reorder):
         s = inv = s_ref = inv_ref = None
     q4, k4, v4 = hf.quantize_qkv(to_dev(w.q), to_dev(w.k), to_dev(w.v), Hkv=w.Hkv,
                                  smooth=w.smooth, s=s, inv_s=inv)
-    out = hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
-                      causal=w.causal, smooth=w.smooth, reorder=reorder, kv_tile=kt)
+    # both Q paths: pre-quantized by the quantize pass (the benchmark's step) and binary16 Q
+    # smoothed and quantized inside the attention kernel
+    qarg = dict(q_f16=to_dev(w.q), s=s) if raw_q else {}
+    out = hf.attn_fwd(None if raw_q else q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q,
+                      N_kv=w.N_kv, d=w.d, causal=w.causal, smooth=w.smooth, reorder=reorder,
+                      kv_tile=kt, **qarg)
     torch.cuda.synchronize()
     rq = oracle.quantize_rows(w.q, w.Hkv, s_ref)
     rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
@@ -88,8 +94,9 @@ def test_prefill_full_size(hf, name, reorder):
     npk = oracle.padded(w.N_kv)
     phat = hf.MX4(torch.zeros((total, npk // 2), dtype=torch.uint8, device="cuda"),
                   torch.zeros((total, npk // 32), dtype=torch.uint8, device="cuda"))
-    hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
-                causal=w.causal, smooth=w.smooth, reorder=reorder, kv_tile=kt, phat=phat)
+    hf.attn_fwd(None if raw_q else q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q,
+                N_kv=w.N_kv, d=w.d, causal=w.causal, smooth=w.smooth, reorder=reorder, kv_tile=kt,
+                phat=phat, **qarg)
     torch.cuda.synchronize()
     pc, ps = to_host(phat.codes[idx]), to_host(phat.scales[idx])
     # compare only the key range each row visits (entries of tiles a row never visits

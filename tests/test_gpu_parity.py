@@ -158,6 +158,55 @@ def test_prefill_matches_oracle(hf, name, kw, reorder, kv_tile):
     assert emax <= ERR_MAX and emean <= ERR_MEAN
 
 
+RAW_Q_CASES = [
+    # name, overrides, reorder, kv_tile (query rows per KV head > 32: the prefill kernel)
+    ("qwen3_8b", dict(B=1, Hq=8, Hkv=2, N=300, d=128, n_cal=96), 1, 128),
+    ("qwen3_8b", dict(B=2, Hq=4, Hkv=2, N=77, N_kv=200, d=128, n_cal=64), 0, 64),  # ragged
+    ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=160, d=256, n_cal=64), 1, 64),
+    ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1, 128),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=100, d=128), 1, 128),            # no Smooth-QK
+]
+
+
+@pytest.mark.parametrize("name,kw,reorder,kv_tile", RAW_Q_CASES)
+def test_prefill_raw_query_matches_oracle(hf, name, kw, reorder, kv_tile):
+    """Binary16 Q given to the prefill kernel, smoothed and quantized there: the same
+    P_hat and output as the oracle on the oracle's own Q_hat."""
+    import torch
+    print(f"[prefill raw q] {name} {kw} reorder={reorder} kv_tile={kv_tile}", flush=True)
+    w = synth.WORKLOADS[name](**kw)
+    if w.smooth:
+        s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    else:
+        s_ref = inv_ref = None
+    rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
+    k4, v4 = mx4_to_dev(rk), v_to_dev(rv)
+    npk = oracle.padded(w.N_kv)
+    phat = hf.MX4(torch.zeros((w.B, w.Hq, w.N_q, npk // 2), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((w.B, w.Hq, w.N_q, npk // 32), dtype=torch.uint8, device="cuda"))
+    out = hf.attn_fwd(None, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
+                      causal=w.causal, smooth=w.smooth, reorder=reorder, phat=phat,
+                      kv_tile=kv_tile, q_f16=to_dev(w.q),
+                      s=None if s_ref is None else to_dev(s_ref))
+    _sync()
+    ref = oracle.attn(w.B, w.Hq, w.Hkv, w.N_q, w.N_kv, w.d, causal=w.causal, reorder=reorder,
+                      kv_tile=kv_tile, q4=rq, k4=rk, v4=rv, want_phat=True)
+    got = to_host(out).reshape(-1, w.d)
+    frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
+    sc = np.mean(to_host(phat.scales).reshape(len(got), -1) == ref["phat_scales"])
+    emax, emean = out_error(got, ref["out"].view(np.float16))
+    print(f"  P_hat code match {frac:.6f}, scale match {sc:.6f}, err max {emax:.2e} mean {emean:.2e}")
+    assert frac >= CODE_MATCH and sc >= CODE_MATCH
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
+    # the same launch with pre-quantized Q gives the same output bit for bit
+    q4d, _, _ = hf.quantize_qkv(to_dev(w.q), None, None, Hkv=w.Hkv, smooth=w.smooth,
+                                s=None if s_ref is None else to_dev(s_ref))
+    out2 = hf.attn_fwd(q4d, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
+                       causal=w.causal, smooth=w.smooth, reorder=reorder, kv_tile=kv_tile)
+    _sync()
+    assert np.array_equal(to_host(out2).view(np.uint16), to_host(out).view(np.uint16))
+
+
 def test_prefill_deterministic(hf):
     w = synth.qwen3_8b(B=1, Hq=4, Hkv=1, N=256, d=128, n_cal=64)
     a, _, _ = _prefill_case(hf, w, 1, dump=False)
