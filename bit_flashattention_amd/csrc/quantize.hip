@@ -93,34 +93,42 @@ __device__ __forceinline__ void quant_row_block(const uint16_t* __restrict__ x, 
 // 256): each lane loads 8 channels (16 bytes, so a wavefront reads 1 KB
 // contiguous per instruction), the block max is combined over the lane quad
 // with DPP, and each lane writes its 4 code bytes; lane 0 of the quad writes
-// the scale byte.  A thread takes NPT such quad slots, t4 = t4_first + j *
-// stride (stride a multiple of 256, so a quad stays a quad), and issues all
-// its loads before converting any, to keep NPT loads in flight per lane.
+// the scale byte.  A workgroup covers ROWS consecutive rows of one (b, h)
+// (ROWS divides the 128-row padding unit, so no workgroup straddles two heads
+// and no per-element division is needed); each thread takes NPT quad slots
+// j * 256 + tid and issues all their loads before converting any.
+template <int D, int NPT>
+struct RowQuads {
+  static constexpr int SLOTS_PER_ROW = 4 * (D / 32);
+  static constexpr int ROWS = 256 * NPT / SLOTS_PER_ROW;
+  static_assert(128 % ROWS == 0, "a workgroup's rows stay inside one head");
+};
+
 template <int D, int NPT>
 __device__ __forceinline__ void quant_row_quads(const uint16_t* __restrict__ x, const float* __restrict__ mult,
-                                                int64_t H, int64_t G, int64_t N, int64_t Npad,
-                                                int64_t t4_first, int64_t stride, int64_t total,
+                                                int64_t H, int64_t G, int64_t N, int64_t Npad, int64_t wg,
                                                 uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  constexpr int64_t per_row = D / 32;
-  const int q = (int)(t4_first & 3);
+  using RQ = RowQuads<D, NPT>;
+  const int64_t wgs_per_head = Npad / RQ::ROWS;
+  const int64_t bh = wg / wgs_per_head;  // uniform: one division per workgroup
+  const int64_t n0 = (wg % wgs_per_head) * RQ::ROWS;
+  const float* mrow = mult ? mult + ((bh % H) / G) * D : nullptr;
+  const uint16_t* xh = x + bh * N * D;
+  uint8_t* ch = codes + (bh * Npad + n0) * (D / 2);
+  uint8_t* sh = scales + (bh * Npad + n0) * (D / 32);
+  const int tid = threadIdx.x, q = tid & 3;
   u32x4 raw[NPT];
   float4 m0[NPT], m1[NPT];
-  int64_t rowv[NPT], blkv[NPT];
-  bool live[NPT];
 #pragma unroll
   for (int j = 0; j < NPT; j++) {
-    const int64_t t4 = t4_first + j * stride;
-    const int64_t block = t4 >> 2;
-    rowv[j] = block / per_row;
-    blkv[j] = block % per_row;
-    const int64_t bh = rowv[j] / Npad, n = rowv[j] % Npad;
-    live[j] = t4 < total && n < N;  // the same for the whole quad
+    const int s = j * 256 + tid;
+    const int r = s / RQ::SLOTS_PER_ROW, blk = (s / 4) % (D / 32);
     raw[j] = u32x4{0u, 0u, 0u, 0u};
     m0[j] = m1[j] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-    if (live[j]) {
-      raw[j] = *reinterpret_cast<const u32x4*>(x + (bh * N + n) * D + blkv[j] * 32 + q * 8);
-      if (mult) {
-        const float4* mp = reinterpret_cast<const float4*>(mult + ((bh % H) / G) * D + blkv[j] * 32 + q * 8);
+    if (n0 + r < N) {
+      raw[j] = *reinterpret_cast<const u32x4*>(xh + (n0 + r) * D + blk * 32 + q * 8);
+      if (mrow) {
+        const float4* mp = reinterpret_cast<const float4*>(mrow + blk * 32 + q * 8);
         m0[j] = mp[0];
         m1[j] = mp[1];
       }
@@ -128,14 +136,16 @@ __device__ __forceinline__ void quant_row_quads(const uint16_t* __restrict__ x, 
   }
 #pragma unroll
   for (int j = 0; j < NPT; j++) {
-    const int64_t t4 = t4_first + j * stride;
+    const int s = j * 256 + tid;
+    const int r = s / RQ::SLOTS_PER_ROW, blk = (s / 4) % (D / 32);
+    const bool live = n0 + r < N;  // the same for the whole quad
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       v[2 * i] = half_to_float((uint16_t)(raw[j][i] & 0xFFFFu));
       v[2 * i + 1] = half_to_float((uint16_t)(raw[j][i] >> 16));
     }
-    if (mult) {
+    if (mrow) {
       v[0] = v[0] * m0[j].x; v[1] = v[1] * m0[j].y; v[2] = v[2] * m0[j].z; v[3] = v[3] * m0[j].w;
       v[4] = v[4] * m1[j].x; v[5] = v[5] * m1[j].y; v[6] = v[6] * m1[j].z; v[7] = v[7] * m1[j].w;
     }
@@ -143,17 +153,15 @@ __device__ __forceinline__ void quant_row_quads(const uint16_t* __restrict__ x, 
 #pragma unroll
     for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
     amax = quad_max(amax);
-    if (t4 < total) {
-      uint32_t out = 0u;
-      uint8_t sc = 0;
-      if (live[j]) {
-        const int e = mx_exponent(amax);
-        out = pack8_fp4(v, pow2f(e));
-        sc = (uint8_t)(e + 127);
-      }
-      *reinterpret_cast<uint32_t*>(codes + rowv[j] * (D / 2) + blkv[j] * 16 + q * 4) = out;
-      if (q == 0) scales[rowv[j] * (D / 32) + blkv[j]] = sc;
+    uint32_t out = 0u;
+    uint8_t sc = 0;
+    if (live) {
+      const int e = mx_exponent(amax);
+      out = pack8_fp4(v, pow2f(e));
+      sc = (uint8_t)(e + 127);
     }
+    *reinterpret_cast<uint32_t*>(ch + r * (D / 2) + blk * 16 + q * 4) = out;
+    if (q == 0) sh[r * (D / 32) + blk] = sc;
   }
 }
 
@@ -228,8 +236,7 @@ struct QuantArgs {
   const uint16_t* x[2];  // Q, K (NULL: none)
   const float* mult[2];  // s, inv_s (NULL: no Smooth-QK multiply)
   int64_t H[2], G[2], N[2], Npad[2];
-  int64_t threads[2];  // quad slots: 4 per 32-channel block
-  int64_t blocks[2];   // workgroups, each covering 256 * kQuadsPerThread slots
+  int64_t blocks[2];   // workgroups, each covering RowQuads::ROWS rows of one (b, h)
   uint8_t* codes[2];
   uint8_t* scales[2];
   const uint16_t* v;
@@ -253,8 +260,7 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
   for (int i = 0; i < 2; i++) {
     if (b < a.blocks[i]) {
       quant_row_quads<D, kQuadsPerThread>(a.x[i], a.mult[i], a.H[i], a.G[i], a.N[i], a.Npad[i],
-                                          b * 256 + threadIdx.x, a.blocks[i] * 256, a.threads[i],
-                                          a.codes[i], a.scales[i]);
+                                          b, a.codes[i], a.scales[i]);
       return;
     }
     b -= a.blocks[i];
@@ -312,8 +318,10 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
     a.G[i] = Hs[i] / Hkv;
     a.N[i] = Ns[i];
     a.Npad[i] = pad_tokens(Ns[i]);
-    a.threads[i] = xs[i] ? 4 * B * Hs[i] * a.Npad[i] * (d / 32) : 0;  // 4 lanes per block
-    a.blocks[i] = (a.threads[i] + 256 * kQuadsPerThread - 1) / (256 * kQuadsPerThread);
+    // workgroups of RowQuads<d, kQuadsPerThread>::ROWS rows: 256 * kQuadsPerThread
+    // quad slots, 4 per 32-channel block
+    const int64_t rows_per_wg = 256 * kQuadsPerThread / (4 * (d / 32));
+    a.blocks[i] = xs[i] ? B * Hs[i] * (a.Npad[i] / rows_per_wg) : 0;
     a.codes[i] = cs[i];
     a.scales[i] = ss[i];
   }
