@@ -392,7 +392,7 @@ def main():
                          "for hardware byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the library has no "
               "multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 

@@ -94,7 +94,7 @@ __device__ __forceinline__ void store_k_block(const AppendArgs& a, int64_t row, 
 }
 
 template <int D>
-__device__ void append_k_pair(const AppendArgs& a, int64_t bg, int64_t t, int pb) {
+__device__ void append_k_pair(const AppendArgs& a, int64_t bg, int64_t g, int64_t t, int pb) {
   constexpr int HALF = D / 2;
   const int64_t p = a.pos + t;
   const uint16_t* src = a.k + (bg * a.T + t) * D;
@@ -116,7 +116,7 @@ __device__ void append_k_pair(const AppendArgs& a, int64_t bg, int64_t t, int pb
     }
   }
   if (a.inv_s) {
-    const float* m = a.inv_s + (bg % a.Hkv) * D + j0;
+    const float* m = a.inv_s + g * D + j0;
     float ml[32], mh[32];
     load32_f32(m, ml);
     load32_f32(m + HALF, mh);
@@ -181,9 +181,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.y < a.chunks_k) {
     // K blocks, dealt over the K chunks
-    const int64_t stride = 256LL * a.chunks_k;
+    const int64_t stride = 256LL * a.chunks_k, g = bg % a.Hkv;
     for (int64_t i = (int64_t)blockIdx.y * 256 + tid; i < a.n_k; i += stride)
-      append_k_pair<D>(a, bg, i / (D / 64), (int)(i % (D / 64)));
+      append_k_pair<D>(a, bg, g, i / (D / 64), (int)(i % (D / 64)));
     return;
   }
   // V tiles, dealt over the V chunks
