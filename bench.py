@@ -74,6 +74,21 @@ def default_kv_tile(d: int) -> int:
     return 128 if d <= 128 else 64
 
 
+def launch_stats(fn, torch, n=100):
+    """Median, p10 and p90 (ms) of `n` launches of fn, each bracketed by its own pair of events
+    on the launch stream (the events add a little to each launch)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)), "launches": n}
+
+
 def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=False):
     """Time `steps` full steps, then `steps` attention launches alone.  A step runs the
     Smooth-QK + quantize pass over Q, K and V, then the attention kernel; with raw_q the
@@ -113,6 +128,7 @@ def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=F
         attn()
     e1.record()
     torch.cuda.synchronize()
+    st["launch_stats"] = launch_stats(attn, torch)
     return ms, e0.elapsed_time(e1) / steps, st
 
 
@@ -152,7 +168,14 @@ def run_decode(w, hf, torch, steps, warmup, copies=2):
     e1.record()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    return ms, e0.elapsed_time(e1) / steps, dict(q=q, s=s, caches=caches, out=out)
+    cnt = [0]
+
+    def one():
+        step(cnt[0])
+        cnt[0] += 1
+    stats = launch_stats(one, torch)
+    return ms, e0.elapsed_time(e1) / steps, dict(q=q, s=s, caches=caches, out=out,
+                                                 launch_stats=stats)
 
 
 def append_bytes(w, T, pos):
@@ -336,6 +359,24 @@ def cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0=None, target_s=12.0, seed=777):
         res["parity_sample"]["gpu_reorder_off_vs_fp64_exact_max"] = float(e0.max())
         res["parity_sample"]["gpu_reorder_off_vs_fp64_exact_mean"] = float(e0.mean())
 
+    # the oracle on one thread: the single-head case whole, and 4 of the 64 sequences of the
+    # decode step (same per-row work)
+    single = {}
+    import synth
+    for name, wk in (("single_head", synth.single_head()), ("decode_4_of_64_sequences",
+                                                           synth.decode(B=4))):
+        s3, i3 = oracle.calibrate(wk.q_cal, wk.k_cal, wk.alpha)
+        q3 = oracle.quantize_rows(wk.q, wk.Hkv, s3)
+        k3 = oracle.quantize_rows(wk.k, wk.Hkv, i3)
+        v3 = oracle.quantize_v(wk.v)
+        t0 = time.perf_counter()
+        oracle.attn(wk.B, wk.Hq, wk.Hkv, wk.N_q, wk.N_kv, wk.d, causal=wk.causal, reorder=1,
+                    kv_tile=wk.kv_tile, num_splits=wk.num_splits, q4=q3, k4=k3, v4=v3, threads=1)
+        dt3 = time.perf_counter() - t0
+        single[name] = {"seconds": dt3, "tflops": wk.flops / dt3 / 1e12,
+                        "kv_gbs": wk.kv_bytes / dt3 / 1e9}
+    res["cpu_oracle_single_thread"] = single
+
     if eps_inputs is not None:
         we, erows, codes, scales = eps_inputs
         s2 = i2 = None
@@ -474,7 +515,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP4_PEAK_TFLOPS, 5),
                      "traffic": traffic, "kernel_ms": round(attn_ms, 5)},
     }
-    extra = {}
+    extra = {"qwen3_8b_attention_per_launch": st["launch_stats"]}
     gpu_out = None if a.no_cpu else st["out"].reshape(-1, w.d).cpu().numpy()
     del st
     eps_inputs = gpu_out_r0 = None
@@ -513,7 +554,8 @@ def main():
         gbs = wd.kv_bytes / (attnd * 1e-3) / 1e9
         extra["decode"] = {"workload": "decode B=64 Hq=32 Hkv=8 d=128 N_kv=8192 splits=16",
                            "kv_bytes": wd.kv_bytes, "ms_per_step": msd, "kernel_ms": attnd,
-                           "kv_gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+                           "kv_gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                           "per_launch": std["launch_stats"]}
         log(f"[bench] decode: {attnd:.4f} ms, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
         del std
         torch.cuda.empty_cache()
@@ -542,6 +584,8 @@ def main():
         log(f"[bench] parity on {ps['rows']} sampled rows: max {ps['err_max']:.2e} mean "
             f"{ps['err_mean']:.2e}; vs fp64 exact attention (GPU): max "
             f"{ps['gpu_vs_fp64_exact_max']:.2e} mean {ps['gpu_vs_fp64_exact_mean']:.2e}")
+        for k, v in cl.get("cpu_oracle_single_thread", {}).items():
+            log(f"[bench] cpu oracle, one thread, {k}: {v['seconds']:.2f} s")
         if "eps_bar" in cl:
             eb = cl["eps_bar"]
             log(f"[bench] eps_bar over {eb['tiles']} tiles: median {eb['median']:.4f}, "
