@@ -290,3 +290,39 @@ def test_empty_and_single_key(hf):
     hf.attn_fwd(mx4_to_dev(rq), mx4_to_dev(rk), v_to_dev(rv), B=1, Hq=2, Hkv=1, N_q=0,
                 N_kv=1, d=128, causal=False, smooth=False, reorder=True, out=empty)
     _sync()
+
+
+def test_maximum_kv_length(hf):
+    """N_kv = 32768, the largest length the FP16 normalizer allows (l <= 1.5 N_kv < 65504):
+    causal prefill over the whole length on sampled rows (the last row attends to every key)
+    and a split-KV decode step over it."""
+    import torch
+    n = hf.MAX_NKV
+    w = synth.qwen3_8b(B=1, Hq=2, Hkv=1, N=n, d=128, n_cal=128)
+    print(f"[max N_kv] N={n}", flush=True)
+    s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
+    k4, v4 = mx4_to_dev(rk), v_to_dev(rv)
+    out = hf.attn_fwd(mx4_to_dev(rq), k4, v4, B=1, Hq=2, Hkv=1, N_q=n, N_kv=n, d=128,
+                      causal=True, smooth=True, reorder=True, kv_tile=128)
+    _sync()
+    rng = np.random.default_rng(32768)
+    rows = np.unique(np.concatenate([rng.choice(2 * n, 40, replace=False), [n - 1, 2 * n - 1]]))
+    ref = oracle.attn(1, 2, 1, n, n, 128, causal=True, reorder=1, kv_tile=128, q4=rq, k4=rk,
+                      v4=rv, rows=rows.astype(np.int64))
+    idx = torch.from_numpy(rows).cuda()
+    emax, emean = out_error(to_host(out.reshape(-1, 128)[idx]), ref["out"].view(np.float16))
+    print(f"  prefill rows {len(rows)}: err max {emax:.2e} mean {emean:.2e}", flush=True)
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
+    # decode: one query per head against all 32768 keys, 16 splits
+    q1 = np.ascontiguousarray(w.q[:, :, -1:])
+    rq1 = oracle.quantize_rows(q1, 1, s_ref)
+    out1 = hf.attn_fwd(None, k4, v4, B=1, Hq=2, Hkv=1, N_q=1, N_kv=n, d=128, causal=False,
+                       smooth=True, reorder=True, q_f16=to_dev(q1), s=to_dev(s_ref),
+                       num_splits=16)
+    _sync()
+    ref1 = oracle.attn(1, 2, 1, 1, n, 128, causal=False, reorder=1, num_splits=16, kv_tile=64,
+                       q4=rq1, k4=rk, v4=rv)
+    emax, emean = out_error(to_host(out1).reshape(-1, 128), ref1["out"].view(np.float16))
+    print(f"  decode: err max {emax:.2e} mean {emean:.2e}", flush=True)
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
