@@ -495,6 +495,24 @@ struct LdsV {
   }
 };
 
+// The same operands read into registers up front (the reads overlap the softmax).
+template <int D, int KT>
+struct LdsVRegs {
+  uint4 va[KT / 64][D / 32];
+  uint32_t vs[D / 32];
+  __device__ __forceinline__ explicit LdsVRegs(const uint8_t* st) {
+    const LdsV<D, KT> l{st};
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ct++) {
+#pragma unroll
+      for (int u = 0; u < KT / 64; u++) va[u][ct] = l.a(u, ct);
+      vs[ct] = l.sc(ct);
+    }
+  }
+  __device__ __forceinline__ uint4 a(int u, int ct) const { return va[u][ct]; }
+  __device__ __forceinline__ uint32_t sc(int ct) const { return vs[ct]; }
+};
+
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   using S = Stage<D, KT>;
@@ -581,18 +599,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     if (t + 1 < tiles) dma_tile<D, KT>(plan, kb0 + KT, nxt);
     if (wave_active && kb0 <= wave_last_key) {
       v16f sacc[NB];
+      uint4 ka[NB][KS];
+      uint32_t ksw[NB][SW];
 #pragma unroll
       for (int bb = 0; bb < NB; bb++) {
-        uint4 ka[KS];
 #pragma unroll
         for (int s = 0; s < KS; s++)
-          ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
-        uint32_t ksw[SW];
-        row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
-        sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
+          ka[bb][s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
+        row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw[bb]);
       }
+#pragma unroll
+      for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(ka[bb], ksw[bb], qb, qsc);
       const bool need_mask = (kb0 + KT - 1) > wave_lim;
-      LdsV<D, KT> vops{st};
+      LdsVRegs<D, KT> vops(st);
       softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
     }
     __syncthreads();
