@@ -11,7 +11,11 @@ Also reported (one JSON line, extra keys): the dominant kernel against the FP4
 MFMA roofline, the other prefill shapes, P-Reordering off, the split-KV decode
 step in GB/s against HBM, and the CPU oracle timed on a sample of rows.
 
+Each measurement first runs its workload untimed for --device-warmup-ms (default 100 ms) so
+that the GPU clocks have ramped up, then W untimed warmup steps, then exactly K timed steps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu] [--decode-only]
+                       [--append-only] [--device-warmup-ms MS]
 """
 from __future__ import annotations
 
@@ -74,6 +78,22 @@ def default_kv_tile(d: int) -> int:
     return 128 if d <= 128 else 64
 
 
+DEVICE_WARMUP_MS = 100.0
+
+
+def device_warmup(fn, torch, ms=None):
+    """Run fn untimed for at least `ms` milliseconds of wall clock before the warmup steps:
+    the GPU raises its clocks over the first tens of milliseconds of sustained work (measured:
+    the Qwen3-8B step goes from 102 to 89 us over the first ~300 steps), and the timed steps
+    should see the sustained rate."""
+    ms = DEVICE_WARMUP_MS if ms is None else ms
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 def launch_stats(fn, torch, n=100):
     """Median, p10 and p90 (ms) of `n` launches of fn, each bracketed by its own pair of events
     on the launch stream (the events add a little to each launch)."""
@@ -112,6 +132,7 @@ def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=F
                         inv_s=st["inv"], out=(None if raw_q else q4, k4, v4))
         attn()
 
+    device_warmup(step, torch)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -156,6 +177,12 @@ def run_decode(w, hf, torch, steps, warmup, copies=2):
                     causal=False, smooth=True, reorder=True, q_f16=q, s=s,
                     num_splits=w.num_splits, out=out, workspace=ws)
 
+    cnt0 = [0]
+
+    def warm():
+        step(cnt0[0])
+        cnt0[0] += 1
+    device_warmup(warm, torch)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -211,6 +238,7 @@ def run_append(w, hf, torch, steps, warmup, T):
     def step():
         hf.kv_append(cache, kn, vn, pos=pos, rope_cos=cos, rope_sin=sin, smooth=True, inv_s=inv)
 
+    device_warmup(step, torch, ms=20.0)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -418,6 +446,7 @@ def cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0=None, target_s=12.0, seed=777):
 
 
 def main():
+    global DEVICE_WARMUP_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -426,12 +455,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decode step (profiling runs); prints its own line")
+    ap.add_argument("--device-warmup-ms", type=float, default=DEVICE_WARMUP_MS,
+                    help="untimed sustained work before the warmup steps of each measurement, "
+                         "so that the GPU clocks have ramped up (0: none)")
     ap.add_argument("--append-only", action="store_true",
                     help="only the KV-cache appends (profiling runs); prints its own line")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference "
                          "for hardware byte counters)")
     a = ap.parse_args()
+    DEVICE_WARMUP_MS = a.device_warmup_ms
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the library has no "
               "multi-GPU path).", file=sys.stderr)
@@ -505,6 +538,7 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4",
         "data": "synthetic (seeded SplitMix64/Box-Muller, RoPE, outlier channels; no model weights)",
+        "device_warmup_ms": DEVICE_WARMUP_MS,
         "config": {"workload": "qwen3_8b_prefill", "B": 1, "Hq": 32, "Hkv": 8, "N": 4096, "d": 128,
                    "causal": True, "smooth_alpha": 0.5, "reorder": True,
                    "kv_tile": default_kv_tile(w.d),
