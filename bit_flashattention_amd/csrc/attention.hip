@@ -82,13 +82,6 @@ __device__ __forceinline__ v16f pv_mfma(int u, const uint4& a, int sa, const uin
   }
 }
 
-// Block exponent of P_hat from the block's largest valid score (bmax = -inf:
-// no valid key, -127): e = clamp(floor(fma(bmax, c, -m)) - 2, -127, 127).
-__device__ __forceinline__ int phat_exponent(float bmax, float c, float m_use) {
-  const float ef = __builtin_amdgcn_fmed3f(floorf(__builtin_fmaf(bmax, c, -m_use)) - 2.0f, -127.0f, 127.0f);
-  return (int)ef;
-}
-
 // Four E2M1 code bytes (8 values, value i in nibble i) of S^T registers
 // r0..r0+7 of one block, RNE(x / sc).
 __device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
@@ -152,17 +145,15 @@ __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool 
     for (int r = 2; r < 16; r++) x = fmaxf(x, s[bb][r]);
     pm[bb] = x;
   }
-  // mine[u]: max of block 2u + hf (the block this lane holds after the code
-  // exchange); oth[u]: max of block 2u + 1 - hf
-  float mine[NU], oth[NU];
+  // full block maxima: a swap of a value with itself hands every lane the
+  // partial max of both halves of its query's block
+  float bm[NB];
   float rmax = kNegInf;
 #pragma unroll
-  for (int u = 0; u < NU; u++) {
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[2 * u]), __float_as_uint(pm[2 * u + 1]), false, false);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[2 * u + 1]), __float_as_uint(pm[2 * u]), false, false);
-    mine[u] = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    oth[u] = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-    rmax = fmaxf(rmax, fmaxf(mine[u], oth[u]));
+  for (int bb = 0; bb < NB; bb++) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[bb]), __float_as_uint(pm[bb]), false, false);
+    bm[bb] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    rmax = fmaxf(rmax, bm[bb]);
   }
 
   // running max (log2 domain, FP16 state)
@@ -171,18 +162,21 @@ __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool 
   const float m_use = (m_new == kNegInf) ? 0.0f : m_new;  // column with no valid key yet
   const float alpha = exp2_hw(m - m_use);
 
-  // per-block exponents; sc[bb]: the scale of block bb for this lane's elements
+  // per-block exponents e = floor(t_max) - 2 with the clamp at -127 applied as
+  // t_max >= -125 (t_max <= half an FP16 ulp of m, so e never reaches 127):
+  // sc[bb] = 2^e scales this lane's elements of block bb; psc[u] is the scale
+  // byte of block 2u + hf, the block this lane holds after the code exchange
   float sc[NB];
+  int fl[NB];
   int* psc = tp.psc;
 #pragma unroll
-  for (int u = 0; u < NU; u++) {
-    const int em = phat_exponent(mine[u], c, m_use);
-    const int eo = phat_exponent(oth[u], c, m_use);
-    const float sm = pow2f(em), so = pow2f(eo);
-    sc[2 * u] = hf ? so : sm;
-    sc[2 * u + 1] = hf ? sm : so;
-    psc[u] = em + 127;
+  for (int bb = 0; bb < NB; bb++) {
+    fl[bb] = (int)floorf(fmaxf(__builtin_fmaf(bm[bb], c, -m_use), -125.0f));
+    sc[bb] = __builtin_amdgcn_ldexpf(0.25f, fl[bb]);
   }
+  const int hmask = -hf;  // all ones in the upper half-wave
+#pragma unroll
+  for (int u = 0; u < NU; u++) psc[u] = ((fl[2 * u + 1] & hmask) | (fl[2 * u] & ~hmask)) + 125;
 
   // P = 2^(S c - m)
 #pragma unroll
