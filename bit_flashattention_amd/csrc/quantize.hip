@@ -194,15 +194,22 @@ __device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, int
   const int64_t tiles = Npad / 64;
   const int64_t bh = tile / tiles, t64 = tile % tiles;  // tile = (b*H + h) * tiles + tile index
   const int tid = threadIdx.x;
-  // load 64 rows x D channels: D/8 16-byte pieces per row
-  constexpr int PIECES = 64 * D / 8;
+  // load 64 rows x D channels (D/8 16-byte pieces per row); every load is
+  // issued before the first LDS store, so the tile costs one memory round
+  // trip per thread, not one per piece
+  constexpr int PER_THREAD = 64 * D / 8 / 256;
+  u32x4 val[PER_THREAD];
 #pragma unroll
-  for (int i = tid; i < PIECES; i += 256) {
-    const int r = i / (D / 8), c8 = i % (D / 8);
+  for (int k = 0; k < PER_THREAD; k++) {
+    const int i = tid + 256 * k, r = i / (D / 8), c8 = i % (D / 8);
     const int64_t n = t64 * 64 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (n < N) val = *reinterpret_cast<const u32x4*>(v + (bh * N + n) * D + c8 * 8);
-    *reinterpret_cast<u32x4*>(&tile_lds[r * ROW + c8 * 8]) = val;
+    val[k] = u32x4{0u, 0u, 0u, 0u};
+    if (n < N) val[k] = *reinterpret_cast<const u32x4*>(v + (bh * N + n) * D + c8 * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < PER_THREAD; k++) {
+    const int i = tid + 256 * k, r = i / (D / 8), c8 = i % (D / 8);
+    *reinterpret_cast<u32x4*>(&tile_lds[r * ROW + c8 * 8]) = val[k];
   }
   __syncthreads();
   // (block, channel) pairs: 2 * D of them; a wavefront reads 64 consecutive
