@@ -1031,7 +1031,9 @@ inline size_t decode_lds_bytes(const KParams& kp, int d) {
 
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool QRAW>
 hipError_t launch_split_t(const KParams& kp, hipStream_t stream) {
-  if (kp.num_splits > 1) {
+  // the fused kernel runs one workgroup per (b, g): it needs enough of them to
+  // fill the chip; fewer take one wavefront per chunk and a separate merge
+  if (kp.num_splits > 1 && kp.B * kp.Hkv >= 128) {
     if (const size_t lds = decode_lds_bytes(kp, D)) {
       attn_decode_kernel<D, KT, CAUSAL, REORDER, DUMP, QRAW>
           <<<dim3((unsigned)(kp.B * kp.Hkv)), dim3(256), lds, stream>>>(kp);

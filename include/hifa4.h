@@ -144,7 +144,11 @@ typedef struct {
   int kv_tile;
   /* Split-KV: 1 = one pass; C > 1 deals the ceil(N_kv/kv_tile) tiles to C
    * chunks of consecutive tiles, each run from (-inf, 0, 0) and merged in
-   * chunk order with FP16 (m, l).  C > 1 requires N_q * Hq/Hkv <= 32. */
+   * chunk order with FP16 (m, l).  C > 1 requires N_q * Hq/Hkv <= 32.
+   * With B * Hkv >= 128 the chunks of a KV head share one workgroup and
+   * merge on chip; with fewer, each chunk is a wavefront of its own and the
+   * merge runs as a second kernel, so small batches want more chunks (one
+   * 32768-token sequence: 32 to 64). */
   int num_splits;
   /* Optional P_hat dump (NULL = off): codes [B][Hq][N_q][Npad_kv/2] and
    * scales [B][Hq][N_q][Npad_kv/32] of every tile a row visits; entries of

@@ -230,6 +230,10 @@ DECODE_CASES = [
     dict(B=3, Hq=32, Hkv=8, N_kv=512, d=128, num_splits=1, kv_tile=64),
     dict(B=2, Hq=4, Hkv=4, N_kv=700, d=64, num_splits=3, kv_tile=64),
     dict(B=1, Hq=8, Hkv=1, N_kv=4096, d=256, num_splits=16, kv_tile=64),
+    # at least 128 (b, g) pairs: the fused decode kernel (partials merged in LDS)
+    dict(B=16, Hq=32, Hkv=8, N_kv=700, d=128, num_splits=5, kv_tile=64),
+    dict(B=32, Hq=16, Hkv=4, N_kv=520, d=256, num_splits=3, kv_tile=64),
+    dict(B=64, Hq=8, Hkv=2, N_kv=300, d=64, num_splits=2, kv_tile=128),
 ]
 
 
