@@ -94,7 +94,8 @@ __device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
 }
 
 // The online-softmax step of one tile of KT keys given its S^T blocks:
-// running max, P, P_hat, normalizer, O rescale and O^T += V_hat^T P_hat^T.
+// running max, P, P_hat, normalizer, O rescale and O^T += V_hat^T P_hat^T
+// (softmax_quant, rescale_o and pv_accumulate below, composed by softmax_pv).
 // vops.a(u, ct) / vops.sc(ct) supply the V_hat operands (byte u of the scale
 // word is unit u's block).  lim: last valid key of this lane's query column.
 //
@@ -102,10 +103,11 @@ __device__ __forceinline__ uint32_t cvt8(const v16f& x, int r0, float sc) {
 // of the key index equal to hf (S^T accumulator register r: key 8(r/4) + 4hf
 // + r%4).  All per-element work runs on these registers in place; the lanes of
 // a pair (q, 0) / (q, 1) exchange only each block's partial max (one
-// permlane32 swap per value) and the packed codes (one swap per two dwords),
+// permlane32 swap per block) and the packed codes (one swap per two dwords),
 // after which lane (q, hf) holds the full 32-code block 2u + hf of unit u --
 // the B operand of the PV product -- with its keys in the operand order
 // operand_key (the V_hat tiled layout stores tokens in the same order).
+
 // One tile's quantized probabilities, between the softmax and the PV product.
 template <int KT>
 struct TileP {
