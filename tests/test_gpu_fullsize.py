@@ -32,9 +32,9 @@ def hf():
     return m
 
 
-def bench_kv_tile(d):
-    # the benchmark's choice: 128-key tiles where supported (d <= 128), else 64
-    return 128 if d <= 128 else 64
+def bench_kv_tile(d, n_kv):
+    # the benchmark's choice: 128-key tiles for d <= 128 over long key ranges, else 64
+    return 128 if d <= 128 and n_kv >= 4096 else 64
 
 
 def sample_rows(total, n_q, seed):
@@ -58,7 +58,7 @@ def check_quantized(got, ref, v_layout=False):
 def test_prefill_full_size(hf, name, reorder, raw_q):
     import torch
     w = synth.WORKLOADS[name]()
-    kt = bench_kv_tile(w.d)
+    kt = bench_kv_tile(w.d, w.N_kv)
     print(f"[fullsize] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N_q} d={w.d} reorder={reorder} "
           f"kv_tile={kt} raw_q={raw_q}", flush=True)
     if w.smooth:
