@@ -230,9 +230,9 @@ hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv
   a.pos = pos;
   a.cap = cap;
   a.n_k = k ? T * (d / 64) : 0;
-  // separate workgroups for K (one block per thread) and V (one 64-position
-  // tile each), so a short append's two round trips overlap; at most 128 of
-  // each per (b, g)
+  // separate workgroups for K (one RoPE block pair per thread) and V (one
+  // 64-position tile each), so a short append's two round trips overlap; at
+  // most 128 of each per (b, g)
   const int64_t tiles = v ? (pos + T - 1) / 64 - pos / 64 + 1 : 0;
   const int64_t ck = (a.n_k + 255) / 256;
   a.chunks_k = (int)(ck > 128 ? 128 : ck);
