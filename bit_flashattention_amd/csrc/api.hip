@@ -192,8 +192,7 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   if (!supported_d(d)) return fail(HIFA4_EUNSUPPORTED, "attn: d = %lld not built (64, 128, 256)", (long long)d);
   if (B == 0 || N_q == 0) return ok();  // nothing to compute
   const int kv_tile = a->kv_tile == 0 ? hifa4::kKvTile : a->kv_tile;
-  if (kv_tile != 64 && !(kv_tile == 128 && d <= 128))
-    return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64 (or 128 with d <= 128)");
+  if (kv_tile != 64 && kv_tile != 128) return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64 or 128");
   if (a->num_splits < 1) return fail(HIFA4_EINVAL, "attn: num_splits must be >= 1");
   const bool q4 = a->q_codes || a->q_scales;
   if (q4 == (a->q_f16 != nullptr)) return fail(HIFA4_EINVAL, "attn: set exactly one of q codes/scales or q_f16");
@@ -209,6 +208,8 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   // decode-shaped calls (a few query rows per KV head) take the split-KV kernels,
   // the rest the prefill kernel; both quantize a raw binary16 Q themselves
   const bool split_path = a->num_splits > 1 || (a->q_f16 != nullptr && G * N_q <= hifa4::kRowsPerWave);
+  if (split_path && kv_tile == 128 && d > 128)
+    return fail(HIFA4_EUNSUPPORTED, "attn: split-KV with d = 256 needs kv_tile 64");
   if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 16) ||
       !aligned(a->v_scales, 16) ||
       (a->q_codes && (!aligned(a->q_codes, 16) || !aligned(a->q_scales, 8))) ||

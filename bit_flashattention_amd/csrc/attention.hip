@@ -595,20 +595,38 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
     if (t + 1 < tiles) dma_tile<D, KT>(plan, kb0 + KT, nxt);
     if (wave_active && kb0 <= wave_last_key) {
       v16f sacc[NB];
-      uint4 ka[NB][KS];
-      uint32_t ksw[NB][SW];
-#pragma unroll
-      for (int bb = 0; bb < NB; bb++) {
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-          ka[bb][s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
-        row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw[bb]);
-      }
-#pragma unroll
-      for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(ka[bb], ksw[bb], qb, qsc);
       const bool need_mask = (kb0 + KT - 1) > wave_lim;
-      LdsVRegs<D, KT> vops(st);
-      softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
+      if constexpr (D * KT <= 128 * 128) {
+        // all K_hat operands read before the S MFMAs, all V_hat operands before the softmax
+        uint4 ka[NB][KS];
+        uint32_t ksw[NB][SW];
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++) {
+#pragma unroll
+          for (int s = 0; s < KS; s++)
+            ka[bb][s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
+          row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw[bb]);
+        }
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(ka[bb], ksw[bb], qb, qsc);
+        LdsVRegs<D, KT> vops(st);
+        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
+      } else {
+        // d = 256 with 128-key tiles: the operands would not fit in registers
+        // next to O (128) and S^T (64), so they are read block by block
+#pragma unroll
+        for (int bb = 0; bb < NB; bb++) {
+          uint4 ka[KS];
+          uint32_t ksw[SW];
+#pragma unroll
+          for (int s = 0; s < KS; s++)
+            ka[s] = *reinterpret_cast<const uint4*>(st + S::KC_OFF + (bb * KS + s) * 1024 + lane * 16);
+          row_scales<D>(st + S::KSC_OFF + (32 * bb + l32) * (D / 32), hf, ksw);
+          sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
+        }
+        const LdsV<D, KT> vops{st};
+        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
+      }
     }
     __syncthreads();
   };
@@ -1124,9 +1142,7 @@ hipError_t dispatch_split(const AttnLaunch& a, const KParams& kp, hipStream_t st
 
 template <int D>
 hipError_t dispatch_prefill_kt(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
-  if constexpr (D <= 128) {
-    if (a.kv_tile == 128) return dispatch_prefill<D, 128>(a, kp, st);
-  }
+  if (a.kv_tile == 128) return dispatch_prefill<D, 128>(a, kp, st);
   return dispatch_prefill<D, 64>(a, kp, st);
 }
 

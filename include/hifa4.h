@@ -39,7 +39,8 @@
  * - Errors: argument checks run first, on the host, and touch no device:
  *   HIFA4_EINVAL (bad sizes, NULL where a buffer is required, misaligned
  *   pointers), HIFA4_EUNSUPPORTED (valid but not built: d not 64/128/256,
- *   kv_tile other than 64, or 128 with d <= 128).  Then HIFA4_ENODEV if no HIP device is visible,
+ *   kv_tile other than 64 or 128, split-KV with d = 256 and kv_tile 128).
+ *   Then HIFA4_ENODEV if no HIP device is visible,
  *   HIFA4_EINVAL for a pointer that is not device memory, HIFA4_ENOSPACE for a
  *   too-small workspace, HIFA4_EHIP if a launch fails.  hifa4_last_error()
  *   returns a thread-local message for the last failing call.  No C++
@@ -139,8 +140,9 @@ typedef struct {
   /* Scratch for split-KV partial states; hifa4_attn_workspace_bytes(). */
   void* workspace;
   size_t workspace_bytes;
-  /* Keys per tile: 64, or 128 when d <= 128 (the tile partition fixes the
-   * FP16 state's rounding sequence).  0 selects the default, 64. */
+  /* Keys per tile: 64 or 128 (the tile partition fixes the FP16 state's
+   * rounding sequence); the split-KV path takes 128 only with d <= 128.
+   * 0 selects the default, 64. */
   int kv_tile;
   /* Split-KV: 1 = one pass; C > 1 deals the ceil(N_kv/kv_tile) tiles to C
    * chunks of consecutive tiles, each run from (-inf, 0, 0) and merged in

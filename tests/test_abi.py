@@ -78,7 +78,7 @@ def _args(hf, **kw):
     (dict(N_q=300, N_kv=256, causal=1), "EINVAL"),
     (dict(d=100), "EINVAL"),
     (dict(d=96), "EUNSUPPORTED"),
-    (dict(args=dict(kv_tile=128), d=256), "EUNSUPPORTED"),
+    (dict(args=dict(kv_tile=128, num_splits=2), d=256, N_q=4), "EUNSUPPORTED"),  # split-KV, d = 256
     (dict(args=dict(kv_tile=96)), "EUNSUPPORTED"),
     (dict(args=dict(num_splits=0)), "EINVAL"),
     (dict(args=dict(q_f16=0x2000)), "EINVAL"),          # both Q forms given

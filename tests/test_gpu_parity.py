@@ -112,6 +112,8 @@ ATTN_CASES = [
     ("qwen3_8b", dict(B=1, Hq=2, Hkv=2, N=200, N_kv=330, d=128, n_cal=64), 1, 64),  # ragged
     ("qwen3_8b", dict(B=1, Hq=2, Hkv=2, N=200, N_kv=330, d=128, n_cal=64), 1, 128),
     ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=384, d=256, n_cal=128), 1, 64),
+    ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=384, d=256, n_cal=128), 1, 128),
+    ("gemma2_9b", dict(B=1, Hq=4, Hkv=2, N=200, N_kv=330, d=256, n_cal=64), 0, 128),  # ragged
     ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 1, 64),
     ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 0, 128),
     ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1, 64),
@@ -163,6 +165,7 @@ RAW_Q_CASES = [
     ("qwen3_8b", dict(B=1, Hq=8, Hkv=2, N=300, d=128, n_cal=96), 1, 128),
     ("qwen3_8b", dict(B=2, Hq=4, Hkv=2, N=77, N_kv=200, d=128, n_cal=64), 0, 64),  # ragged
     ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=160, d=256, n_cal=64), 1, 64),
+    ("gemma2_9b", dict(B=1, Hq=2, Hkv=1, N=160, d=256, n_cal=64), 1, 128),
     ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1, 128),
     ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=100, d=128), 1, 128),            # no Smooth-QK
 ]
