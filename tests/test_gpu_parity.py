@@ -118,6 +118,10 @@ ATTN_CASES = [
     ("llama_batched", dict(B=2, Hq=4, Hkv=2, N=257, d=128), 0, 128),
     ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 1, 64),
     ("qwen3_8b", dict(B=1, Hq=8, Hkv=1, N=130, d=64, n_cal=64), 0, 128),
+    # non-causal with N_q != N_kv: fewer queries than keys, and more (ragged tails on both)
+    ("qwen3_8b", dict(B=1, Hq=4, Hkv=2, N=200, N_kv=330, d=128, n_cal=64, causal=False), 1, 128),
+    ("llama_batched", dict(B=2, Hq=4, Hkv=1, N=300, N_kv=100, d=64, causal=False), 0, 64),
+    ("gemma2_9b", dict(B=1, Hq=2, Hkv=2, N=97, N_kv=161, d=256, n_cal=64, causal=False), 1, 128),
 ]
 
 
@@ -146,9 +150,13 @@ def _prefill_case(hf, w, reorder, dump=True, kv_tile=64):
 @pytest.mark.parametrize("name,kw,reorder,kv_tile", ATTN_CASES)
 def test_prefill_matches_oracle(hf, name, kw, reorder, kv_tile):
     print(f"[prefill] {name} {kw} reorder={reorder} kv_tile={kv_tile}", flush=True)
+    kw = dict(kw)
+    causal = kw.pop("causal", None)
     w = synth.WORKLOADS[name](**kw)
     if name == "single_head":
         w.causal = False
+    if causal is not None:
+        w.causal = causal
     out, phat, ref = _prefill_case(hf, w, reorder, kv_tile=kv_tile)
     got = to_host(out).reshape(-1, w.d).view(np.uint16)
     frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
