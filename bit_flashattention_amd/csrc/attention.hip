@@ -985,32 +985,38 @@ __global__ __launch_bounds__(256, (D * KT <= 128 * 64) ? 2 : 1) void attn_decode
 // ---------------------------------------------------------------------------
 // Merge of split partials, in chunk order: M = max m_k, w_k = 2^(m_k - M),
 // L = sum w_k l_k, A = sum w_k O_k (fp32, sequential), out = fp16(A / fp16(L)).
-// One thread per (row, 4 channels): 16-byte partial loads, 8-byte stores.
+// One workgroup of d threads per query row, thread c owning channel c.  M is
+// reduced over the workgroup first (a max is exact in any order); the sums then
+// run over the chunks in order, in batches of 16 whose loads are all issued
+// before the batch is summed, so a long chunk list is not walked one latency at
+// a time.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws_o,
-                                                         const float* __restrict__ ws_ml,
-                                                         int64_t rows, int d, int C,
+                                                         const float* __restrict__ ws_ml, int C,
                                                          uint16_t* __restrict__ out) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int q = d / 4;
-  if (t >= rows * q) return;
-  const int64_t row = t / q;
-  const int c4 = (int)(t % q);
+  __shared__ float wmax[4];
+  const int64_t row = blockIdx.x;
+  const int d = (int)blockDim.x, c = (int)threadIdx.x;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml + row * C * 2);
   float M = kNegInf;
-  for (int k = 0; k < C; k++) M = fmaxf(M, ml[k].x);
-  float L = 0.0f;
-  float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  // partials in groups of 8: the group's loads are all issued before its
-  // (in-order) accumulation
-  constexpr int GRP = 8;
+  for (int k = c; k < C; k += d) M = fmaxf(M, ml[k].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((c & 63) == 0) wmax[c >> 6] = M;
+  __syncthreads();
+  M = wmax[0];
+  for (int w = 1; w < d / 64; w++) M = fmaxf(M, wmax[w]);
+
+  const float* o = ws_o + row * C * d + c;
+  float L = 0.0f, A = 0.0f;
+  constexpr int GRP = 16;
   for (int k0 = 0; k0 < C; k0 += GRP) {
-    float4 o[GRP];
+    float ov[GRP];
     float2 st[GRP];
 #pragma unroll
     for (int j = 0; j < GRP; j++) {
       if (k0 + j < C) {
-        o[j] = *reinterpret_cast<const float4*>(ws_o + (row * C + k0 + j) * d + 4 * c4);
+        ov[j] = o[(int64_t)(k0 + j) * d];
         st[j] = ml[k0 + j];
       }
     }
@@ -1020,16 +1026,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
         const float w = (st[j].x == kNegInf) ? 0.0f : exp2_hw(st[j].x - M);
         const float wl = w * st[j].y;
         L = L + wl;
-        const float wo[4] = {w * o[j].x, w * o[j].y, w * o[j].z, w * o[j].w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) A[i] = A[i] + wo[i];
+        const float wo = w * ov[j];
+        A = A + wo;
       }
     }
   }
   const float lf = round_f16(L);
-  const uint32_t lo = (uint32_t)float_to_half_bits(A[0] / lf) | ((uint32_t)float_to_half_bits(A[1] / lf) << 16);
-  const uint32_t hi = (uint32_t)float_to_half_bits(A[2] / lf) | ((uint32_t)float_to_half_bits(A[3] / lf) << 16);
-  *reinterpret_cast<uint2*>(out + row * d + 4 * c4) = make_uint2(lo, hi);
+  out[row * d + c] = float_to_half_bits(A / lf);
 }
 
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
@@ -1066,9 +1069,7 @@ hipError_t launch_split_t(const KParams& kp, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || kp.num_splits == 1) return e;
   const int64_t rows = kp.B * kp.Hq * kp.N_q;
-  const int64_t n = rows * (D / 4);
-  attn_merge_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
-      kp.ws_o, kp.ws_ml, rows, D, kp.num_splits, kp.out);
+  attn_merge_kernel<<<dim3((unsigned)rows), dim3(D), 0, stream>>>(kp.ws_o, kp.ws_ml, kp.num_splits, kp.out);
   return hipGetLastError();
 }
 

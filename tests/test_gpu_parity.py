@@ -245,6 +245,9 @@ DECODE_CASES = [
     dict(B=16, Hq=32, Hkv=8, N_kv=700, d=128, num_splits=5, kv_tile=64),
     dict(B=32, Hq=16, Hkv=4, N_kv=520, d=256, num_splits=3, kv_tile=64),
     dict(B=64, Hq=8, Hkv=2, N_kv=300, d=64, num_splits=2, kv_tile=128),
+    # one sequence, many chunks: the merge kernel over more chunks than channels
+    dict(B=1, Hq=4, Hkv=1, N_kv=8192, d=64, num_splits=128, kv_tile=64),
+    dict(B=1, Hq=8, Hkv=2, N_kv=16384, d=128, num_splits=64, kv_tile=128),
 ]
 
 
