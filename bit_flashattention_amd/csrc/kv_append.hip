@@ -14,9 +14,9 @@
 //      that adds to it; those values wait in a caller-owned staging buffer
 //      [B][Hkv][32][d] until the block is full.
 //
-// Work split (grid = B*Hkv x (K chunks + V chunks), 256 threads): K block
-// pairs (one token row x the 32 channels of a block and of its RoPE partner,
-// one thread each) are dealt over the K chunks;
+// Work split (grid = B*Hkv x (K chunks + V chunks), 256 threads): K octets
+// (one token row x 8 channels of the first half and their 8 RoPE partners, one
+// lane each, four lanes per MX block pair) are dealt over the K chunks;
 // V is handled per 64-position tile, staged through LDS by a whole V-chunk
 // workgroup.  Only V chunk 0 of a (b, g) reads the staging buffer (in the first
 // touched tile, which holds the positions before the call) and only it writes
@@ -40,34 +40,9 @@ struct AppendArgs {
   uint8_t* v_scales;      //                    [B][Hkv][cap/64][d][2]
   uint16_t* stage;        // [B][Hkv][32][d] binary16
   int64_t Hkv, T, pos, cap;
-  int64_t n_k;            // K items: T * d/64 pairs of 32-channel blocks
+  int64_t n_k;            // K items: T * d/16 octets of RoPE channel pairs
   int chunks_k, chunks_v; // workgroups per (b, g) for K and for V
 };
-
-__device__ __forceinline__ void load32_f16(const uint16_t* p, float (&x)[32]) {
-  const u32x4* src = reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const u32x4 raw = src[u];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      x[8 * u + 2 * i] = half_to_float((uint16_t)(raw[i] & 0xFFFFu));
-      x[8 * u + 2 * i + 1] = half_to_float((uint16_t)(raw[i] >> 16));
-    }
-  }
-}
-
-__device__ __forceinline__ void load32_f32(const float* p, float (&x)[32]) {
-  const float4* src = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int u = 0; u < 8; u++) {
-    const float4 f = src[u];
-    x[4 * u] = f.x;
-    x[4 * u + 1] = f.y;
-    x[4 * u + 2] = f.z;
-    x[4 * u + 3] = f.w;
-  }
-}
 
 // One MX block of 32 values: 16 code bytes (value i in nibble i) and the scale byte.
 __device__ __forceinline__ void mx32(const float (&x)[32], u32x4& codes, uint8_t& scale) {
@@ -81,54 +56,75 @@ __device__ __forceinline__ void mx32(const float (&x)[32], u32x4& codes, uint8_t
   scale = (uint8_t)(e + 127);
 }
 
-// K: token t of the call, the channel blocks [32 pb, 32 pb + 32) and its RoPE
-// partner [32 pb + d/2, 32 pb + d/2 + 32): both rows of each rotated pair come
-// from one load of each half and one table row.
-__device__ __forceinline__ void store_k_block(const AppendArgs& a, int64_t row, int blk, int D,
-                                              const float (&x)[32]) {
-  u32x4 codes;
-  uint8_t sc;
-  mx32(x, codes, sc);
-  *reinterpret_cast<u32x4*>(a.k_codes + row * (D / 2) + 16 * blk) = codes;
-  a.k_scales[row * (D / 32) + blk] = sc;
-}
-
+// K: token t of the call, lane octet o: channels [8o, 8o + 8) of the first
+// half and their RoPE partners [d/2 + 8o, d/2 + 8o + 8).  The four lanes of an
+// aligned quad (o = 4b' .. 4b' + 3) hold MX block b' and its partner block
+// d/64 + b': each lane loads 16 contiguous bytes of each half (consecutive lanes
+// read consecutive bytes), the block maxima are combined over the quad with
+// DPP, and each lane writes its 4 code bytes of each block (lane 0 of the quad
+// the scale bytes).  Every item of a quad has the same token, so a quad is
+// either entirely in range or entirely out.
 template <int D>
-__device__ void append_k_pair(const AppendArgs& a, int64_t bg, int64_t g, int64_t t, int pb) {
+__device__ __forceinline__ void append_k_oct(const AppendArgs& a, int64_t bg, int64_t g, int64_t t, int o) {
   constexpr int HALF = D / 2;
   const int64_t p = a.pos + t;
   const uint16_t* src = a.k + (bg * a.T + t) * D;
-  const int j0 = 32 * pb;
-  float lo[32], hi[32];
-  load32_f16(src + j0, lo);
-  load32_f16(src + j0 + HALF, hi);
+  const int j0 = 8 * o;
+  const u32x4 rl = *reinterpret_cast<const u32x4*>(src + j0);
+  const u32x4 rh = *reinterpret_cast<const u32x4*>(src + HALF + j0);
+  float lo[8], hi[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    lo[2 * i] = half_to_float((uint16_t)(rl[i] & 0xFFFFu));
+    lo[2 * i + 1] = half_to_float((uint16_t)(rl[i] >> 16));
+    hi[2 * i] = half_to_float((uint16_t)(rh[i] & 0xFFFFu));
+    hi[2 * i + 1] = half_to_float((uint16_t)(rh[i] >> 16));
+  }
   if (a.cos_t) {
     // rotate-half: r[j] = x[j] c - x[j + d/2] s, r[j + d/2] = x[j + d/2] c + x[j] s,
     // each product and each sum one fp32 rounding, r kept as binary16
-    float c[32], s[32];
-    load32_f32(a.cos_t + p * HALF + j0, c);
-    load32_f32(a.sin_t + p * HALF + j0, s);
+    const float4* cp = reinterpret_cast<const float4*>(a.cos_t + p * HALF + j0);
+    const float4* sp = reinterpret_cast<const float4*>(a.sin_t + p * HALF + j0);
+    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
-      const float ac = lo[i] * c[i], bs = hi[i] * s[i], bc = hi[i] * c[i], as = lo[i] * s[i];
+    for (int i = 0; i < 8; i++) {
+      const float ac = lo[i] * c[i], bs = hi[i] * sn[i], bc = hi[i] * c[i], as = lo[i] * sn[i];
       lo[i] = half_to_float(float_to_half_bits(ac - bs));
       hi[i] = half_to_float(float_to_half_bits(bc + as));
     }
   }
   if (a.inv_s) {
-    const float* m = a.inv_s + g * D + j0;
-    float ml[32], mh[32];
-    load32_f32(m, ml);
-    load32_f32(m + HALF, mh);
+    const float4* mp = reinterpret_cast<const float4*>(a.inv_s + g * D + j0);
+    const float4* mq = reinterpret_cast<const float4*>(a.inv_s + g * D + HALF + j0);
+    const float4 m0 = mp[0], m1 = mp[1], n0 = mq[0], n1 = mq[1];
+    const float ml[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    const float mh[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
+    for (int i = 0; i < 8; i++) {
       lo[i] = lo[i] * ml[i];
       hi[i] = hi[i] * mh[i];
     }
   }
+  float al = 0.0f, ah = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    al = fmaxf(al, fabsf(lo[i]));
+    ah = fmaxf(ah, fabsf(hi[i]));
+  }
+  al = quad_max(al);
+  ah = quad_max(ah);
+  const int el = mx_exponent(al), eh = mx_exponent(ah);
   const int64_t row = bg * a.cap + p;
-  store_k_block(a, row, pb, D, lo);
-  store_k_block(a, row, pb + HALF / 32, D, hi);
+  const int blk = o / 4, q = o % 4;
+  uint8_t* crow = a.k_codes + row * (D / 2);
+  *reinterpret_cast<uint32_t*>(crow + 16 * blk + 4 * q) = pack8_fp4(lo, pow2f(el));
+  *reinterpret_cast<uint32_t*>(crow + 16 * (blk + HALF / 32) + 4 * q) = pack8_fp4(hi, pow2f(eh));
+  if (q == 0) {
+    a.k_scales[row * (D / 32) + blk] = (uint8_t)(el + 127);
+    a.k_scales[row * (D / 32) + blk + HALF / 32] = (uint8_t)(eh + 127);
+  }
 }
 
 // V: the touched 32-position blocks of 64-position tile tau.  The workgroup
@@ -183,7 +179,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     // K blocks, dealt over the K chunks
     const int64_t stride = 256LL * a.chunks_k, g = bg % a.Hkv;
     for (int64_t i = (int64_t)blockIdx.y * 256 + tid; i < a.n_k; i += stride)
-      append_k_pair<D>(a, bg, g, i / (D / 64), (int)(i % (D / 64)));
+      append_k_oct<D>(a, bg, g, i / (D / 16), (int)(i % (D / 16)));
     return;
   }
   // V tiles, dealt over the V chunks
@@ -229,10 +225,10 @@ hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv
   a.T = T;
   a.pos = pos;
   a.cap = cap;
-  a.n_k = k ? T * (d / 64) : 0;
-  // separate workgroups for K (one RoPE block pair per thread) and V (one
-  // 64-position tile each), so a short append's two round trips overlap; at
-  // most 128 of each per (b, g)
+  a.n_k = k ? T * (d / 16) : 0;
+  // separate workgroups for K (one octet of RoPE channel pairs per thread) and
+  // V (one 64-position tile each), so a short append's two round trips overlap;
+  // at most 128 of each per (b, g)
   const int64_t tiles = v ? (pos + T - 1) / 64 - pos / 64 + 1 : 0;
   const int64_t ck = (a.n_k + 255) / 256;
   a.chunks_k = (int)(ck > 128 ? 128 : ck);
