@@ -190,14 +190,18 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     // the first touched tile: its older positions come from the staging buffer
     append_v_tile<D>(a, bg, tau0, lds);
     // every read of the staging buffer is done: keep the new tokens of the
-    // block that is still filling
+    // block that is still filling.  When that block lies in the tile just
+    // quantized, its rows are still in LDS (no second trip to memory).
     if (end % 32 != 0) {
       const int64_t first = end / 32 * 32 > a.pos ? end / 32 * 32 : a.pos;
+      const bool in_lds = (end - 1) / 64 == tau0;
       for (int64_t i = tid; i < (end - first) * (D / 8); i += 256) {
         const int64_t n = first + i / (D / 8);
         const int c8 = (int)(i % (D / 8));
-        *reinterpret_cast<u32x4*>(a.stage + (bg * 32 + (n & 31)) * D + c8 * 8) =
-            *reinterpret_cast<const u32x4*>(a.v + (bg * a.T + (n - a.pos)) * D + c8 * 8);
+        const u32x4 val =
+            in_lds ? *reinterpret_cast<const u32x4*>(&lds[(n - 64 * tau0) * (D + 8) + c8 * 8])
+                   : *reinterpret_cast<const u32x4*>(a.v + (bg * a.T + (n - a.pos)) * D + c8 * 8);
+        *reinterpret_cast<u32x4*>(a.stage + (bg * 32 + (n & 31)) * D + c8 * 8) = val;
       }
     }
   }
