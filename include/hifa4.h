@@ -148,9 +148,10 @@ typedef struct {
    * chunks of consecutive tiles, each run from (-inf, 0, 0) and merged in
    * chunk order with FP16 (m, l).  C > 1 requires N_q * Hq/Hkv <= 32.
    * With B * Hkv >= 128 the chunks of a KV head share one workgroup and
-   * merge on chip; with fewer, each chunk is a wavefront of its own and the
-   * merge runs as a second kernel, so small batches want more chunks (one
-   * 32768-token sequence: 32 to 64). */
+   * merge on chip (when their C * Hq/Hkv * N_q * (d + 2) fp32 partial states
+   * fit in 64 KB of LDS); otherwise each chunk is a wavefront of its own and
+   * the merge runs as a second kernel, so small batches want more chunks (one
+   * 32768-token sequence: about 64). */
   int num_splits;
   /* Optional P_hat dump (NULL = off): codes [B][Hq][N_q][Npad_kv/2] and
    * scales [B][Hq][N_q][Npad_kv/32] of every tile a row visits; entries of
