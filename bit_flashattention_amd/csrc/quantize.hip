@@ -13,26 +13,40 @@ namespace hifa4 {
 
 // ---------------------------------------------------------------------------
 // Calibration maxima: qmax[g][j] = max |Q| over (b, heads of group g, tokens),
-// kmax[g][j] = max |K| over (b, tokens).  One thread per (g, j); the inner
-// loop walks rows, so a wavefront reads contiguous channels of one row.
+// kmax[g][j] = max |K| over (b, tokens).  Grid (channel groups of 64, g, row
+// chunks): lane l of a wavefront owns channel 64 x + l and the four wavefronts
+// of a workgroup walk the chunk's rows (the group's Q rows, then its K rows)
+// four apart, so every load is 128 contiguous bytes of one row.  The lanes'
+// maxima are combined into qmax / kmax (zeroed beforehand) with an integer
+// atomic max on the bit patterns: non-negative floats order as their bits, and
+// a max is exact in any order.  fmaxf drops NaN inputs, as a sequential scan
+// with fmaxf would.
 // ---------------------------------------------------------------------------
-__global__ void calib_absmax_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-                                    float* __restrict__ qmax, float* __restrict__ kmax) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= Hkv * d) return;
-  const int64_t g = idx / d, j = idx % d, G = Hq / Hkv;
+__global__ __launch_bounds__(256) void calib_absmax_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t B, int64_t Hq,
+    int64_t Hkv, int64_t N, int64_t d, int rows_per_wg, float* __restrict__ qmax,
+    float* __restrict__ kmax) {
+  const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t g = blockIdx.y, G = Hq / Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nq = B * G * N, nrows = nq + B * N;
+  const int64_t r0 = (int64_t)blockIdx.z * rows_per_wg;
+  if (j >= d) return;
   float qm = 0.0f, km = 0.0f;
-  for (int64_t b = 0; b < B; b++) {
-    for (int64_t h = g * G; h < (g + 1) * G; h++) {
-      const uint16_t* base = q + ((b * Hq + h) * N) * d + j;
-      for (int64_t n = 0; n < N; n++) qm = fmaxf(qm, fabsf(half_to_float(base[n * d])));
+#pragma unroll 4
+  for (int i = wave; i < rows_per_wg; i += 4) {
+    const int64_t r = r0 + i;
+    if (r >= nrows) break;
+    if (r < nq) {
+      const int64_t b = r / (G * N), h = g * G + (r / N) % G, n = r % N;
+      qm = fmaxf(qm, fabsf(half_to_float(q[((b * Hq + h) * N + n) * d + j])));
+    } else {
+      const int64_t rk = r - nq, b = rk / N, n = rk % N;
+      km = fmaxf(km, fabsf(half_to_float(k[((b * Hkv + g) * N + n) * d + j])));
     }
-    const uint16_t* kb = k + ((b * Hkv + g) * N) * d + j;
-    for (int64_t n = 0; n < N; n++) km = fmaxf(km, fabsf(half_to_float(kb[n * d])));
   }
-  qmax[idx] = qm;
-  kmax[idx] = km;
+  if (qm > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(qmax + g * d + j), __float_as_uint(qm));
+  if (km > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(kmax + g * d + j), __float_as_uint(km));
 }
 
 // ---------------------------------------------------------------------------
@@ -281,10 +295,17 @@ hipError_t launch_calib_absmax(const void* q, const void* k, int64_t B, int64_t 
                                int64_t N, int64_t d, float* qmax, float* kmax,
                                hipStream_t stream) {
   const int64_t n = Hkv * d;
-  const int threads = 256;
-  const int64_t blocks = (n + threads - 1) / threads;
-  calib_absmax_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
-      (const uint16_t*)q, (const uint16_t*)k, B, Hq, Hkv, N, d, qmax, kmax);
+  hipError_t e = hipMemsetAsync(qmax, 0, (size_t)n * sizeof(float), stream);
+  if (e == hipSuccess) e = hipMemsetAsync(kmax, 0, (size_t)n * sizeof(float), stream);
+  if (e != hipSuccess) return e;
+  // Q rows then K rows of one group, 64 per workgroup (more when the grid's
+  // z dimension would exceed its limit)
+  const int64_t rows = B * (Hq / Hkv) * N + B * N;
+  int64_t per_wg = 64;
+  while ((rows + per_wg - 1) / per_wg > 65535) per_wg *= 2;
+  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)Hkv, (unsigned)((rows + per_wg - 1) / per_wg));
+  calib_absmax_kernel<<<grid, dim3(256), 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, B, Hq,
+                                                      Hkv, N, d, (int)per_wg, qmax, kmax);
   return hipGetLastError();
 }
 

@@ -65,6 +65,24 @@ def test_calibrate_and_quantize_match_oracle(hf, name, kw):
         assert np.array_equal(to_host(got.scales), ref[1])
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,alpha", [(1, 32, 8, 512, 128, 0.5), (2, 6, 2, 77, 96, 0.25),
+                                                 (3, 4, 4, 300, 256, 0.5), (1, 8, 1, 5000, 64, 1.0)])
+def test_calibrate_shapes(hf, B, Hq, Hkv, N, d, alpha):
+    """Calibration maxima over batches, GQA groups, a channel count that is not a multiple of
+    64 and more rows than one workgroup takes; zero channels give s = 1."""
+    q = synth.tensor(101, B, Hq, N, d)
+    k = synth.tensor(102, B, Hkv, N, d)
+    q[:, :, :, 3] = 0          # zero in Q only
+    k[:, :, :, 5] = 0          # zero in K only
+    q[:, :, :, d - 1] = 0      # zero in both
+    k[:, :, :, d - 1] = 0
+    k[:, :, N - 1, 7] = np.float16(-300.0)  # the maximum on the last K row
+    s, inv = hf.calibrate_smooth(to_dev(q), to_dev(k), alpha)
+    s_ref, inv_ref = oracle.calibrate(q, k, alpha)
+    assert np.array_equal(to_host(s), s_ref) and np.array_equal(to_host(inv), inv_ref)
+    assert np.all(s_ref[:, [3, 5, d - 1]] == 1.0)
+
+
 def test_quantize_edge_values(hf):
     """Zero blocks, subnormal binary16, saturating and tiny blocks."""
     import torch
