@@ -368,13 +368,18 @@ struct KParams {
   int64_t B, Hq, Hkv, N_q, N_kv, Npad_q, Npad_kv;
   int G, num_splits, n_tiles, tiles_per_split;
   int heads_per_wg;  // query heads per prefill workgroup (the rest of its 4 waves are row blocks)
+  int one_round;     // prefill: every workgroup is resident at once (row groups in complementary order)
   float c;
 };
 
 // ---------------------------------------------------------------------------
 // Prefill.  Workgroup = 4 wavefronts on KV head (b, g): nh query heads of the
 // group x (4 / nh) row blocks of 32 rows.  Grid (B * Hkv * G/nh, row groups);
-// row groups run last-first so the longest causal work starts earliest.
+// row groups run last-first so the longest causal work starts earliest and
+// the dispatcher's in-order refill balances the rest.  When the whole grid is
+// resident at once (at most two workgroups per CU) there is no refill: then
+// the first half of the grid runs longest first and the second half shortest
+// first, so the two workgroups that share a CU carry complementary row ranges.
 //
 // LDS stage of one tile (KT keys), all in MFMA operand order:
 //   [K_hat codes: KT/32 blocks x D/64 k-steps x 64 lanes x 16 B]
@@ -525,7 +530,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   const int64_t hc = bgc / (p.B * p.Hkv), bg = bgc % (p.B * p.Hkv);
   const int64_t b = bg / p.Hkv, g = bg % p.Hkv;
   const int64_t h = g * p.G + hc * nh + (wave % nh);
-  const int64_t rgrp = (int64_t)gridDim.y - 1 - blockIdx.y;
+  const int64_t Y = gridDim.y, hy = (Y + 1) / 2, y = blockIdx.y;
+  const int64_t rgrp = (!p.one_round || y < hy) ? Y - 1 - y : y - hy;
   const int64_t wg_row0 = rgrp * 32 * nr;
   const int64_t row0 = wg_row0 + 32 * (wave / nh);
   const int64_t bh = b * p.Hq + h;
@@ -1105,7 +1111,13 @@ hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   // x = (head chunk, b, g) with the KV head fastest: consecutive workgroups
   // land on consecutive XCDs, so each XCD's L2 serves a fixed set of KV heads
   dim3 grid((unsigned)(kp.B * kp.Hkv * (kp.G / nh)), (unsigned)((kp.N_q + 32 * nr - 1) / (32 * nr)));
-  attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP><<<grid, dim3(256), 0, stream>>>(kp);
+  // two workgroups fit on a CU (registers and LDS of every instantiation)
+  int dev = 0, cus = 0;
+  KParams k2 = kp;
+  k2.one_round = hipGetDevice(&dev) == hipSuccess &&
+                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                 (int64_t)grid.x * grid.y <= 2LL * cus;
+  attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP><<<grid, dim3(256), 0, stream>>>(k2);
   return hipGetLastError();
 }
 
@@ -1164,6 +1176,7 @@ KParams make_params(const AttnLaunch& a) {
   kp.n_tiles = (int)((a.N_kv + a.kv_tile - 1) / a.kv_tile);
   kp.tiles_per_split = (kp.n_tiles + a.num_splits - 1) / a.num_splits;
   kp.heads_per_wg = (kp.G % 4 == 0) ? 4 : (kp.G % 2 == 0) ? 2 : 1;
+  kp.one_round = 0;
   kp.c = (float)(1.4426950408889634073599246810019 / __builtin_sqrt((double)a.d));
   return kp;
 }
