@@ -312,6 +312,55 @@ def test_split_path_with_prequantized_q_and_causal(hf):
     assert emax <= ERR_MAX and emean <= ERR_MEAN
 
 
+# Split-KV with 128-key tiles (the split kernel and the merge kernel, fewer than 128 KV heads in
+# the batch): reorder off, a causal mask over several query rows, d = 64, Smooth-QK off, 16 and
+# 24 query columns, no merge (one chunk), one tile per chunk, and merges of 64 chunks (one batch
+# of loads) and 65 (the batched path).
+# (B, Hq, Hkv, N_q, N_kv, d, causal, reorder, raw_q, smooth, num_splits)
+SPLIT_CASES = [
+    (2, 8, 2, 1, 1000, 128, False, True, True, True, 4),
+    (2, 8, 2, 1, 1000, 128, False, False, True, True, 4),
+    (1, 4, 2, 1, 700, 64, False, True, True, True, 3),
+    (2, 8, 2, 4, 700, 128, True, False, False, True, 5),
+    (2, 8, 2, 4, 700, 128, True, True, False, True, 5),
+    (1, 16, 2, 2, 515, 64, True, True, True, False, 2),
+    (1, 16, 2, 3, 515, 128, False, True, True, True, 2),
+    (1, 8, 2, 1, 128, 128, False, True, True, True, 1),
+    (3, 4, 1, 1, 4096, 128, False, True, True, True, 1),
+    (1, 4, 1, 1, 8192, 64, False, False, True, True, 64),
+    (1, 4, 1, 1, 8320, 128, False, True, True, True, 65),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N_q,N_kv,d,causal,reorder,raw_q,smooth,C", SPLIT_CASES)
+def test_split_cases_match_oracle(hf, B, Hq, Hkv, N_q, N_kv, d, causal, reorder, raw_q, smooth, C):
+    import torch
+    print(f"[split] B={B} Hq={Hq} Hkv={Hkv} N_q={N_q} N_kv={N_kv} d={d} causal={causal} "
+          f"reorder={reorder} raw_q={raw_q} smooth={smooth} C={C}", flush=True)
+    w = synth.qwen3_8b(B=B, Hq=Hq, Hkv=Hkv, N=N_q, N_kv=N_kv, d=d, n_cal=64)
+    s_ref = inv_ref = None
+    if smooth:
+        s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    rq, rk, rv = oracle_quant(w, s_ref, inv_ref)
+    npk = oracle.padded(N_kv)
+    phat = hf.MX4(torch.zeros((B, Hq, N_q, npk // 2), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((B, Hq, N_q, npk // 32), dtype=torch.uint8, device="cuda"))
+    qarg = dict(q_f16=to_dev(w.q), s=to_dev(s_ref) if smooth else None) if raw_q else {}
+    out = hf.attn_fwd(None if raw_q else mx4_to_dev(rq), mx4_to_dev(rk), v_to_dev(rv), B=B, Hq=Hq,
+                      Hkv=Hkv, N_q=N_q, N_kv=N_kv, d=d, causal=causal, smooth=smooth,
+                      reorder=reorder, num_splits=C, phat=phat, kv_tile=128, **qarg)
+    _sync()
+    ref = oracle.attn(B, Hq, Hkv, N_q, N_kv, d, causal=causal, reorder=int(reorder), num_splits=C,
+                      kv_tile=128, q4=rq, k4=rk, v4=rv, want_phat=True)
+    got = to_host(out).reshape(-1, d)
+    frac = code_match_fraction(to_host(phat.codes).reshape(len(got), -1), ref["phat_codes"])
+    sfrac = np.mean(to_host(phat.scales).reshape(len(got), -1) == ref["phat_scales"])
+    emax, emean = out_error(got, ref["out"].view(np.float16))
+    print(f"  P_hat code match {frac:.6f}, scale match {sfrac:.6f}, err max {emax:.2e} mean {emean:.2e}")
+    assert frac >= CODE_MATCH and sfrac >= CODE_MATCH
+    assert emax <= ERR_MAX and emean <= ERR_MEAN
+
+
 def test_empty_and_single_key(hf):
     import torch
     w = synth.qwen3_8b(B=1, Hq=2, Hkv=1, N=3, N_kv=1, d=128, n_cal=32)
