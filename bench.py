@@ -595,6 +595,20 @@ def main():
         log(f"[bench] decode: {attnd:.4f} ms, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
         del std
         torch.cuda.empty_cache()
+        # one long sequence: 8 KV heads are too few for the fused decode kernel, so this runs
+        # the split kernel (one wavefront per chunk) and the merge kernel; eight cache copies
+        # (285 MB, more than the last-level cache) so that every launch reads HBM
+        w1 = synth.decode(B=1, N_kv=32768, num_splits=64, n_cal=128)
+        ms1, attn1, st1 = run_decode(w1, hf, torch, a.steps, a.warmup, copies=8)
+        gbs1 = w1.kv_bytes / (attn1 * 1e-3) / 1e9
+        extra["decode_one_sequence"] = {
+            "workload": "decode B=1 Hq=32 Hkv=8 d=128 N_kv=32768 splits=64 kv_tile=64",
+            "kv_bytes": w1.kv_bytes, "ms_per_step": ms1, "kernel_ms": attn1, "kv_gbs": gbs1,
+            "frac_hbm_peak": gbs1 / HBM_PEAK_GBS, "per_launch": st1["launch_stats"]}
+        log(f"[bench] decode, one 32768-token sequence (64 splits): {attn1 * 1e3:.1f} us, "
+            f"{gbs1:.1f} GB/s ({100 * gbs1 / HBM_PEAK_GBS:.1f} % of HBM)")
+        del st1, w1
+        torch.cuda.empty_cache()
         wa = synth.kv_append()
         extra["kv_append"] = {"workload": "kv_append B=64 Hkv=8 d=128: RoPE + Smooth-QK + MXFP4 of "
                                           "the new K rows, V blocks re-quantized, cache of 8192 "
