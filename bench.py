@@ -288,6 +288,32 @@ def sample_rows(w, n, seed=12345):
     return np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
 
 
+def accuracy_rows(w, seed):
+    """Query rows on which the error against fp64 exact attention is reported: every row of a
+    workload of at most 4096 rows (the single head, the decode step), else a seeded 1/16 sample
+    of all rows (every head)."""
+    total = w.B * w.Hq * w.N_q
+    if total <= 4096:
+        return np.arange(total, dtype=np.int64)
+    return sample_rows(w, total // 16, seed=seed)
+
+
+def rows_to_host(out, rows, d, torch):
+    """The given flat query rows of a [B][Hq][N_q][d] binary16 output, as a numpy array."""
+    idx = torch.from_numpy(np.ascontiguousarray(rows)).cuda()
+    return out.reshape(-1, d)[idx].cpu().numpy()
+
+
+def rel_error(got, ref):
+    """(max, mean) of |got - ref| / max_row |ref| (rows of the last axis; fp64)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, ref.shape[-1])
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+    rm = np.abs(r).max(axis=1, keepdims=True)
+    rm[rm == 0] = 1.0
+    e = np.abs(g - r) / rm
+    return float(e.max()), float(e.mean())
+
+
 def row_flops(w, rows):
     i = rows % w.N_q
     keys = (i + w.N_kv - w.N_q + 1) if w.causal else np.full_like(i, w.N_kv)
@@ -306,9 +332,43 @@ def phat_tile_sums(codes, scales, kv_tile):
     return blk.reshape(codes.shape[0], -1, kv_tile // 32).sum(axis=2)
 
 
-def eps_bar_gpu_dump(w, hf, torch, heads, kv_tile=64):
+def eps_bar_tiles(sum_p, sum_phat, n_heads, N_q, rows_per_tile=64):
+    """Per-tile mass change of the P-Reordering diagnostic.  sum_p / sum_phat: [n_heads * N_q][T]
+    per-(row, key tile) sums of P and of P_hat (NaN where the row has no valid key in the tile),
+    rows of each head contiguous.  A tile is rows_per_tile query rows x one key tile; over its
+    rows with at least one valid key (sum P > 0):
+        eps_bar = mean_i (sum P_hat_i - sum P_i) / sum P_i
+        mass-weighted = (sum_i sum P_hat_i - sum_i sum P_i) / sum_i sum P_i
+    Returns (eps_bar, mass_weighted), one entry per tile that has such a row."""
+    T = sum_p.shape[1]
+    valid = np.isfinite(sum_phat) & np.isfinite(sum_p) & (sum_p > 0)
+    shape = (n_heads, N_q // rows_per_tile, rows_per_tile, T)
+    spv = np.where(valid, sum_p, 0.0).reshape(shape)
+    sphv = np.where(valid, sum_phat, 0.0).reshape(shape)
+    val = valid.reshape(shape)
+    eps = np.where(val, (sphv - spv) / np.where(val, spv, 1.0), 0.0)
+    cnt = val.sum(axis=2)
+    tiles = cnt > 0
+    eb = (eps.sum(axis=2) / np.maximum(cnt, 1))[tiles]
+    mw = ((sphv - spv).sum(axis=2) / np.maximum(spv.sum(axis=2), 1e-300))[tiles]
+    return eb, mw
+
+
+def eps_bar_summary(eb, mw, workload):
+    hist, edges = np.histogram(eb, bins=16, range=(-0.2, 0.2))
+    return {"workload": workload, "tiles": int(eb.size),
+            "median": float(np.median(eb)), "mean": float(eb.mean()),
+            "p10": float(np.percentile(eb, 10)), "p90": float(np.percentile(eb, 90)),
+            "fraction_negative": float(np.mean(eb < 0)),
+            "mass_weighted_median": float(np.median(mw)),
+            "histogram": {"edges": [round(x, 4) for x in edges.tolist()], "counts": hist.tolist(),
+                          "below": int(np.sum(eb < -0.2)), "above": int(np.sum(eb > 0.2))}}
+
+
+def eps_bar_gpu_dump(w, hf, torch, kv_tile=64):
     """GPU half of the epsilon-bar diagnostic: one P_hat-dumping launch of the whole workload
-    (off the timed path); returns the dumped rows of the sampled (b, h) heads."""
+    (off the timed path); returns the dump (device tensors, [rows][Npad/2] codes and
+    [rows][Npad/32] scale bytes)."""
     st = prepare_prefill(w, hf, torch)
     q4, k4, v4 = st["bufs"]
     hf.quantize_qkv(st["q"], st["k"], st["v"], Hkv=w.Hkv, smooth=w.smooth, s=st["s"],
@@ -320,36 +380,58 @@ def eps_bar_gpu_dump(w, hf, torch, heads, kv_tile=64):
     hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
                 causal=w.causal, smooth=w.smooth, reorder=True, out=st["out"], kv_tile=kv_tile,
                 phat=phat)
-    rows = (heads[:, None] * w.N_q + np.arange(w.N_q)[None, :]).reshape(-1)
-    idx = torch.from_numpy(rows).cuda()
-    codes, scales = phat.codes[idx].cpu().numpy(), phat.scales[idx].cpu().numpy()
+    torch.cuda.synchronize()
+    codes, scales = phat.codes.cpu().numpy(), phat.scales.cpu().numpy()
     del st, phat
     torch.cuda.empty_cache()
-    return rows, codes, scales
+    return codes, scales
 
 
-def cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0=None, target_s=12.0, seed=777):
+def cpu_info():
+    """Host CPU model and counts (the oracle baseline reports the threads it used)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "cpus_available": affinity}
+
+
+def cpu_leg(w, gpu_out, eps_inputs, acc_inputs, target_s=12.0, seed=777):
     """Everything that runs the CPU oracle, after the GPU measurements:
 
     * the baseline: the oracle's attention forward (quantized operands given, same tile
-      size as the GPU) on a seeded sample of query rows of the primary workload, on the host
-      threads this process may use (at most 16); a first 1024-row pass sizes the sample so
-      that the timed pass takes about `target_s` seconds;
-    * parity of the GPU output on those rows (error relative to each row's max |O_oracle|)
-      and the error of both against fp64 softmax attention on the binary16 inputs (also for
-      the GPU output with P-Reordering off, when given);
+      size as the GPU) on a seeded sample of query rows of the primary workload, on this
+      process's share of the host CPUs (the CPUs it may run on, at most 16: the share one
+      GPU gets on a shared box); a first 1024-row pass sizes the sample so that the timed
+      pass takes about `target_s` seconds;
+    * parity of the GPU output on those rows (error relative to each row's max |O_oracle|);
+    * for every workload in `acc_inputs`, the error of the GPU output and of the oracle's
+      against fp64 softmax attention on the binary16 inputs, on all rows of the small
+      workloads and a seeded 1/16 of the rows of the others, per P-Reordering setting;
     * the epsilon-bar diagnostic: per tile of 64 query rows x 64 keys, the mean over its rows
-      of (sum P_hat - sum P) / sum P, from the oracle's per-tile sums on sampled heads, with
+      of (sum P_hat - sum P) / sum P, from the oracle's per-tile sums over every head, with
       the GPU's dumped P_hat checked to give the same sum P_hat."""
     import oracle
+    import synth
     res = {}
-    s_ref = inv_ref = None
-    if w.smooth:
-        s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
-    rq = oracle.quantize_rows(w.q, w.Hkv, s_ref)
-    rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
-    rv = oracle.quantize_v(w.v)
-    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def quant(wk):
+        s_ref = inv_ref = None
+        if wk.smooth:
+            s_ref, inv_ref = oracle.calibrate(wk.q_cal, wk.k_cal, wk.alpha)
+        return (oracle.quantize_rows(wk.q, wk.Hkv, s_ref), oracle.quantize_rows(wk.k, wk.Hkv, inv_ref),
+                oracle.quantize_v(wk.v))
+
+    rq, rk, rv = quant(w)
+    threads = oracle.cpu_share()
     total = w.B * w.Hq * w.N_q
     kt = default_kv_tile(w.d, w.N_kv)
 
@@ -365,40 +447,43 @@ def cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0=None, target_s=12.0, seed=777):
     n = int(min(total, max(1024, 1024 * target_s * rate / row_flops(w, probe))))
     rows = sample_rows(w, n, seed=seed)
     dt, ref = timed(rows)
-    res["cpu_baseline"] = {
-        "value": row_flops(w, rows) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-        "kind": "oracle",
-        "sample": f"{w.name} attention (quantized operands given, kv_tile {kt}), {len(rows)} "
-                  f"seeded random query rows of {total}, {dt:.1f} s"}
+    res["cpu_baseline"] = dict(
+        value=row_flops(w, rows) / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+        sample=f"{w.name} attention (quantized operands given, kv_tile {kt}), {len(rows)} "
+               f"seeded random query rows of {total}, {dt:.1f} s", **cpu_info())
 
-    got = gpu_out.reshape(-1, w.d)[rows].astype(np.float64)
-    exp = ref["out"].view(np.float16).astype(np.float64)
-    e = np.abs(got - exp) / np.abs(exp).max(axis=1, keepdims=True)
-    sub = rows[:256]
-    exact = oracle.attn_exact(w.q, w.k, w.v, w.causal, rows=sub, threads=threads)
-    ex_max = np.abs(exact).max(axis=1, keepdims=True)
-    eg = np.abs(got[:256] - exact) / ex_max
-    eo = np.abs(exp[:256] - exact) / ex_max
-    res["parity_sample"] = {
-        "rows": len(rows), "err_max": float(e.max()), "err_mean": float(e.mean()),
-        "vs_fp64_exact_rows": len(sub), "gpu_vs_fp64_exact_max": float(eg.max()),
-        "gpu_vs_fp64_exact_mean": float(eg.mean()), "oracle_vs_fp64_exact_max": float(eo.max()),
-        "oracle_vs_fp64_exact_mean": float(eo.mean())}
-    if gpu_out_r0 is not None:
-        e0 = np.abs(gpu_out_r0.reshape(-1, w.d)[sub].astype(np.float64) - exact) / ex_max
-        res["parity_sample"]["gpu_reorder_off_vs_fp64_exact_max"] = float(e0.max())
-        res["parity_sample"]["gpu_reorder_off_vs_fp64_exact_mean"] = float(e0.mean())
+    got = gpu_out.reshape(-1, w.d)[rows]
+    emax, emean = rel_error(got, ref["out"].view(np.float16))
+    res["parity_sample"] = {"workload": w.name, "rows": len(rows), "err_max": emax,
+                            "err_mean": emean}
+
+    # error against fp64 exact attention, every workload
+    acc = {}
+    for name, wk, arows, outs, kw in acc_inputs:
+        q3, k3, v3 = quant(wk)
+        exact = oracle.attn_exact(wk.q, wk.k, wk.v, wk.causal, rows=arows, threads=threads)
+        entry = {"rows": int(len(arows)), "rows_total": int(wk.B * wk.Hq * wk.N_q)}
+        for reorder, gout in outs.items():
+            r3 = oracle.attn(wk.B, wk.Hq, wk.Hkv, wk.N_q, wk.N_kv, wk.d, causal=wk.causal,
+                             reorder=reorder, q4=q3, k4=k3, v4=v3, rows=arows, threads=threads,
+                             **kw)
+            o3 = r3["out"].view(np.float16)
+            tag = "reorder_on" if reorder else "reorder_off"
+            gm, ga = rel_error(gout, exact)
+            om, oa = rel_error(o3, exact)
+            pm, pa = rel_error(gout, o3)
+            entry[tag] = {"gpu_vs_fp64_exact_max": gm, "gpu_vs_fp64_exact_mean": ga,
+                          "oracle_vs_fp64_exact_max": om, "oracle_vs_fp64_exact_mean": oa,
+                          "gpu_vs_oracle_max": pm, "gpu_vs_oracle_mean": pa}
+        acc[name] = entry
+    res["error_vs_fp64_exact"] = acc
 
     # the oracle on one thread: the single-head case whole, and 4 of the 64 sequences of the
     # decode step (same per-row work)
     single = {}
-    import synth
     for name, wk in (("single_head", synth.single_head()), ("decode_4_of_64_sequences",
                                                            synth.decode(B=4))):
-        s3, i3 = oracle.calibrate(wk.q_cal, wk.k_cal, wk.alpha)
-        q3 = oracle.quantize_rows(wk.q, wk.Hkv, s3)
-        k3 = oracle.quantize_rows(wk.k, wk.Hkv, i3)
-        v3 = oracle.quantize_v(wk.v)
+        q3, k3, v3 = quant(wk)
         t0 = time.perf_counter()
         oracle.attn(wk.B, wk.Hq, wk.Hkv, wk.N_q, wk.N_kv, wk.d, causal=wk.causal, reorder=1,
                     kv_tile=wk.kv_tile, num_splits=wk.num_splits, q4=q3, k4=k3, v4=v3, threads=1)
@@ -408,42 +493,31 @@ def cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0=None, target_s=12.0, seed=777):
     res["cpu_oracle_single_thread"] = single
 
     if eps_inputs is not None:
-        we, erows, codes, scales = eps_inputs
-        s2 = i2 = None
-        if we.smooth:
-            s2, i2 = oracle.calibrate(we.q_cal, we.k_cal, we.alpha)
-        q2 = oracle.quantize_rows(we.q, we.Hkv, s2)
-        k2 = oracle.quantize_rows(we.k, we.Hkv, i2)
-        v2 = oracle.quantize_v(we.v)
-        r2 = oracle.attn(we.B, we.Hq, we.Hkv, we.N_q, we.N_kv, we.d, causal=we.causal, reorder=1,
-                         kv_tile=64, q4=q2, k4=k2, v4=v2, rows=erows, want_sums=True,
-                         threads=threads)
-        sp, sph = r2["sum_p"], r2["sum_phat"]
-        T = sp.shape[1]
-        gph = phat_tile_sums(codes, scales, 64)[:, :T]
-        seen = np.isfinite(sph)
-        dev = np.abs(gph[seen] - sph[seen]) / np.maximum(sph[seen], 1e-300)
-        valid = seen & (sp > 0)
-        nh = len(erows) // we.N_q
-        shape = (nh, we.N_q // 64, 64, T)
-        spv = np.where(valid, sp, 0.0).reshape(shape)
-        sphv = np.where(valid, sph, 0.0).reshape(shape)
-        val = valid.reshape(shape)
-        eps = np.where(val, (sphv - spv) / np.where(val, spv, 1.0), 0.0)
-        cnt = val.sum(axis=2)
-        tiles = cnt > 0
-        eb = (eps.sum(axis=2) / np.maximum(cnt, 1))[tiles]
-        mw = ((sphv - spv).sum(axis=2) / np.maximum(spv.sum(axis=2), 1e-300))[tiles]
-        hist, edges = np.histogram(eb, bins=16, range=(-0.2, 0.2))
-        res["eps_bar"] = {
-            "workload": f"{we.name}: {nh} seeded (b, h) heads of {we.B * we.Hq}, tiles of 64 rows "
-                        f"x 64 keys", "tiles": int(tiles.sum()),
-            "median": float(np.median(eb)), "mean": float(eb.mean()),
-            "p10": float(np.percentile(eb, 10)), "p90": float(np.percentile(eb, 90)),
-            "fraction_negative": float(np.mean(eb < 0)), "mass_weighted_median": float(np.median(mw)),
-            "histogram": {"edges": [round(x, 4) for x in edges.tolist()], "counts": hist.tolist(),
-                          "below": int(np.sum(eb < -0.2)), "above": int(np.sum(eb > 0.2))},
-            "gpu_dump_sum_phat_max_rel_dev": float(dev.max()) if dev.size else 0.0}
+        we, codes, scales = eps_inputs
+        q2, k2, v2 = quant(we)
+        heads = we.B * we.Hq
+        chunk = 8  # heads per oracle call
+        ebs, mws, dev_max = [], [], 0.0
+        for h0 in range(0, heads, chunk):
+            h1 = min(heads, h0 + chunk)
+            erows = np.arange(h0 * we.N_q, h1 * we.N_q, dtype=np.int64)
+            r2 = oracle.attn(we.B, we.Hq, we.Hkv, we.N_q, we.N_kv, we.d, causal=we.causal,
+                             reorder=1, kv_tile=64, q4=q2, k4=k2, v4=v2, rows=erows,
+                             want_sums=True, threads=threads)
+            sp, sph = r2["sum_p"], r2["sum_phat"]
+            T = sp.shape[1]
+            gph = phat_tile_sums(codes[erows], scales[erows], 64)[:, :T]
+            seen = np.isfinite(sph)
+            if seen.any():
+                dev = np.abs(gph[seen] - sph[seen]) / np.maximum(sph[seen], 1e-300)
+                dev_max = max(dev_max, float(dev.max()))
+            eb, mw = eps_bar_tiles(sp, sph, h1 - h0, we.N_q)
+            ebs.append(eb)
+            mws.append(mw)
+        eb, mw = np.concatenate(ebs), np.concatenate(mws)
+        res["eps_bar"] = eps_bar_summary(
+            eb, mw, f"{we.name}: all {heads} (b, h) heads, tiles of 64 rows x 64 keys")
+        res["eps_bar"]["gpu_dump_sum_phat_max_rel_dev"] = dev_max
     return res
 
 
@@ -553,9 +627,26 @@ def main():
     }
     extra = {"qwen3_8b_attention_per_launch": st["launch_stats"]}
     gpu_out = None if a.no_cpu else st["out"].reshape(-1, w.d).cpu().numpy()
+    # per workload: (name, workload, rows, {reorder: GPU output rows}, oracle tile settings),
+    # the error against fp64 exact attention is computed on these rows in the CPU leg
+    acc_inputs = []
+    acc_rows = accuracy_rows(w, seed=2)
+    acc_q = {1: gpu_out[acc_rows] if gpu_out is not None else None}
     del st
-    eps_inputs = gpu_out_r0 = None
+    eps_inputs = None
     if not a.quick:
+        # the single-head workload: latency-bound, reported for its error and time
+        w1h = synth.single_head()
+        ms1h, attn1h, st1h = run_prefill(w1h, hf, torch, a.steps, a.warmup, reorder=True, kv_tile=64)
+        extra["single_head"] = {"ms_per_step": ms1h, "attn_ms": attn1h,
+                                "attn_tflops": w1h.flops / (attn1h * 1e-3) / 1e12}
+        log(f"[bench] single head 256x256 d128: step {ms1h * 1e3:.1f} us, attention "
+            f"{attn1h * 1e3:.1f} us")
+        if not a.no_cpu:
+            r1h = accuracy_rows(w1h, seed=1)
+            acc_inputs.append(("single_head", w1h, r1h,
+                               {1: rows_to_host(st1h["out"], r1h, w1h.d, torch)}, dict(kv_tile=64)))
+        del st1h
         msq, attnq, stq = run_prefill(w, hf, torch, a.steps, a.warmup, reorder=True, raw_q=True)
         extra["qwen3_8b_q_in_kernel"] = {"ms_per_step": msq, "attn_ms": attnq,
                                          "step_tflops": w.flops / (msq * 1e-3) / 1e12}
@@ -567,13 +658,19 @@ def main():
                                          "attn_tflops": w.flops / (attn0 * 1e-3) / 1e12}
         log(f"[bench] reorder off: attention {attn0:.4f} ms")
         if not a.no_cpu:
-            gpu_out_r0 = st0["out"].reshape(-1, w.d).cpu().numpy()
+            acc_q[0] = rows_to_host(st0["out"], acc_rows, w.d, torch)
+            acc_inputs.append(("qwen3_8b_prefill", w, acc_rows, acc_q,
+                               dict(kv_tile=default_kv_tile(w.d, w.N_kv))))
         del st0
         for name, fn in (("gemma2_9b_prefill", synth.gemma2_9b),
                          ("llama_batched_prefill", synth.llama_batched)):
             wx = fn()
+            xrows = accuracy_rows(wx, seed=3 if name.startswith("gemma") else 4)
+            xouts = {}
             for reorder in ((True, False) if name.startswith("llama") else (True,)):
                 msx, attnx, stx = run_prefill(wx, hf, torch, a.steps, a.warmup, reorder=reorder)
+                if not a.no_cpu:
+                    xouts[int(reorder)] = rows_to_host(stx["out"], xrows, wx.d, torch)
                 key = name + ("" if reorder else "_reorder_off")
                 extra[key] = {"ms_per_step": msx, "attn_ms": attnx,
                               "step_tflops": wx.flops / (msx * 1e-3) / 1e12,
@@ -582,9 +679,11 @@ def main():
                 log(f"[bench] {key}: step {msx:.4f} ms, attention {attnx:.4f} ms "
                     f"({extra[key]['attn_tflops']:.1f} TFLOP/s)")
                 del stx
+            if not a.no_cpu:
+                acc_inputs.append((name, wx, xrows, xouts,
+                                   dict(kv_tile=default_kv_tile(wx.d, wx.N_kv))))
             if name.startswith("llama") and not a.no_cpu:
-                heads = np.sort(np.random.default_rng(4242).choice(wx.B * wx.Hq, 16, replace=False))
-                eps_inputs = (wx,) + eps_bar_gpu_dump(wx, hf, torch, heads)
+                eps_inputs = (wx,) + eps_bar_gpu_dump(wx, hf, torch)
         wd = synth.decode()
         msd, attnd, std = run_decode(wd, hf, torch, a.steps, a.warmup)
         gbs = wd.kv_bytes / (attnd * 1e-3) / 1e9
@@ -593,6 +692,10 @@ def main():
                            "kv_gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
                            "per_launch": std["launch_stats"]}
         log(f"[bench] decode: {attnd:.4f} ms, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)")
+        if not a.no_cpu:
+            drows = accuracy_rows(wd, seed=5)
+            acc_inputs.append(("decode", wd, drows, {1: rows_to_host(std["out"], drows, wd.d, torch)},
+                               dict(kv_tile=wd.kv_tile, num_splits=wd.num_splits)))
         del std
         torch.cuda.empty_cache()
         # one long sequence: 8 KV heads are too few for the fused decode kernel, so this runs
@@ -626,14 +729,25 @@ def main():
         del wa
         torch.cuda.empty_cache()
     if not a.no_cpu:
-        cl = cpu_leg(w, gpu_out, eps_inputs, gpu_out_r0)
+        if a.quick:
+            acc_inputs.append(("qwen3_8b_prefill", w, acc_rows, {1: acc_q[1]},
+                               dict(kv_tile=default_kv_tile(w.d, w.N_kv))))
+        cl = cpu_leg(w, gpu_out, eps_inputs, acc_inputs)
         result["cpu_baseline"] = cl.pop("cpu_baseline")
         log(f"[bench] cpu oracle: {result['cpu_baseline']['value']:.6f} TFLOP/s on "
             f"{result['cpu_baseline']['cores']} threads ({result['cpu_baseline']['sample']})")
         ps = cl["parity_sample"]
         log(f"[bench] parity on {ps['rows']} sampled rows: max {ps['err_max']:.2e} mean "
-            f"{ps['err_mean']:.2e}; vs fp64 exact attention (GPU): max "
-            f"{ps['gpu_vs_fp64_exact_max']:.2e} mean {ps['gpu_vs_fp64_exact_mean']:.2e}")
+            f"{ps['err_mean']:.2e}")
+        for k, v in cl.get("error_vs_fp64_exact", {}).items():
+            for tag in ("reorder_on", "reorder_off"):
+                if tag in v:
+                    e = v[tag]
+                    log(f"[bench] {k} {tag}, {v['rows']} rows vs fp64 exact: GPU max "
+                        f"{e['gpu_vs_fp64_exact_max']:.3f} mean {e['gpu_vs_fp64_exact_mean']:.4f}; "
+                        f"oracle max {e['oracle_vs_fp64_exact_max']:.3f} mean "
+                        f"{e['oracle_vs_fp64_exact_mean']:.4f}; GPU vs oracle max "
+                        f"{e['gpu_vs_oracle_max']:.1e}")
         for k, v in cl.get("cpu_oracle_single_thread", {}).items():
             log(f"[bench] cpu oracle, one thread, {k}: {v['seconds']:.2f} s")
         if "eps_bar" in cl:

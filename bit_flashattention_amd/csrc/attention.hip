@@ -30,6 +30,8 @@
 //  * Split-KV (decode): one wavefront per (b, KV head, chunk) streams its
 //    chunk from HBM with a one-tile register prefetch; an ordered merge
 //    kernel combines the FP16 (m, l) partial states.
+#include <atomic>
+
 #include "hifa4_device.hpp"
 #include "hifa4_internal.hpp"
 
@@ -1105,6 +1107,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   out[row * d + c] = float_to_half_bits(A / lf);
 }
 
+// Compute units of the current device, queried once per device (0 if unknown).
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   const int nh = kp.heads_per_wg, nr = 4 / nh;
@@ -1112,11 +1128,9 @@ hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   // land on consecutive XCDs, so each XCD's L2 serves a fixed set of KV heads
   dim3 grid((unsigned)(kp.B * kp.Hkv * (kp.G / nh)), (unsigned)((kp.N_q + 32 * nr - 1) / (32 * nr)));
   // two workgroups fit on a CU (registers and LDS of every instantiation)
-  int dev = 0, cus = 0;
+  const int cus = device_cu_count();
   KParams k2 = kp;
-  k2.one_round = hipGetDevice(&dev) == hipSuccess &&
-                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                 (int64_t)grid.x * grid.y <= 2LL * cus;
+  k2.one_round = cus > 0 && (int64_t)grid.x * grid.y <= 2LL * cus;
   attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP><<<grid, dim3(256), 0, stream>>>(k2);
   return hipGetLastError();
 }

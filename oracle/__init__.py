@@ -27,6 +27,16 @@ def padded(n: int) -> int:
     return -(-n // TOKEN_PAD) * TOKEN_PAD
 
 
+def cpu_share() -> int:
+    """Host threads the oracle uses when none are given: the CPUs this process may run on,
+    at most 16 (the host share one GPU gets on a shared box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def build(force: bool = False) -> str:
     """Compile liboracle.so with g++ (no fast-math, no FP contraction)."""
     src = os.path.join(_HERE, "hifa4_oracle.cpp")
@@ -258,7 +268,7 @@ def attn(B, Hq, Hkv, N_q, N_kv, d, *, causal, reorder, kv_tile=64, num_splits=1,
         r = np.ascontiguousarray(rows, dtype=np.int64)
         keep.append(r)
         P.rows, P.n_rows = _p(r), len(r)
-    P.threads = threads
+    P.threads = threads if threads > 0 else cpu_share()
     rc = _load().orc_attn(ctypes.byref(P))
     if rc != 0:
         raise ValueError(f"orc_attn failed with {rc}")
@@ -274,7 +284,7 @@ def attn_exact(q, k, v, causal: bool, rows: Optional[np.ndarray] = None, threads
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     rc = _load().orc_attn_exact(_p(_f16bits(q)), _p(_f16bits(k)), _p(_f16bits(v)), B, Hq, Hkv,
                                 N_q, N_kv, d, int(causal), _p(r), 0 if r is None else len(r),
-                                _p(out), threads)
+                                _p(out), threads if threads > 0 else cpu_share())
     if rc != 0:
         raise ValueError(f"orc_attn_exact failed with {rc}")
     return out

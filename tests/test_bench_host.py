@@ -53,3 +53,71 @@ def test_decode_workload_shape_and_bytes():
     w = synth.Workload("decode", 64, 32, 8, 1, 8192, 128, False, True, 0.5, 64, 16, (1,))
     assert w.kv_bytes == 570_425_344
     assert w.flops == 4 * 8192 * 128 * 32 * 64
+
+
+def _bench():
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench
+
+
+def test_eps_bar_tiles_hand_example():
+    """Two heads of 64 query rows, two key tiles.  Head 0, tile 0: rows with sum P = 2 and
+    sum P_hat = 1.8 (relative change -0.1) except row 5, whose sum P_hat is 2.2 (+0.1); tile 1
+    is masked (NaN) for rows 0..31 and has sum P = 4, sum P_hat = 3 (-0.25) for rows 32..63.
+    Head 1: sum P = 0 in tile 0 (no mass: left out) and -0.5 for every row of tile 1."""
+    import numpy as np
+    b = _bench()
+    sp = np.full((128, 2), 2.0)
+    sph = np.full((128, 2), 1.8)
+    sph[5, 0] = 2.2
+    sp[:32, 1] = np.nan
+    sph[:32, 1] = np.nan
+    sp[32:64, 1], sph[32:64, 1] = 4.0, 3.0
+    sp[64:, 0], sph[64:, 0] = 0.0, 0.0
+    sp[64:, 1], sph[64:, 1] = 2.0, 1.0
+    eb, mw = b.eps_bar_tiles(sp, sph, n_heads=2, N_q=64)
+    # tiles in (head, row tile, key tile) order: (0,0,0), (0,0,1), (1,0,1)
+    assert eb.shape == (3,)
+    assert np.allclose(eb, [(63 * -0.1 + 0.1) / 64, -0.25, -0.5])
+    assert np.allclose(mw, [(63 * 1.8 + 2.2 - 128) / 128, -0.25, -0.5])
+    s = b.eps_bar_summary(eb, mw, "hand")
+    assert s["tiles"] == 3 and s["fraction_negative"] == 1.0
+    assert sum(s["histogram"]["counts"]) + s["histogram"]["below"] + s["histogram"]["above"] == 3
+
+
+def test_phat_tile_sums_hand_example():
+    """One row, 128 keys: block 0 holds code 2 (value 1) at every key with scale byte 127
+    (x1), block 1 code 15 (-6) at key 32 with scale 128 (x2), blocks 2-3 code 1 (0.5) with
+    scale 125 (x1/4).  Tile sums at kv_tile 64: 32 + (-12) = 20 and 64 * 0.5 / 4 = 8."""
+    import numpy as np
+    b = _bench()
+    nib = np.zeros(128, dtype=np.uint8)
+    nib[:32] = 2
+    nib[32] = 15
+    nib[64:] = 1
+    codes = (nib[0::2] | (nib[1::2] << 4)).reshape(1, 64)
+    scales = np.array([[127, 128, 125, 125]], dtype=np.uint8)
+    t = b.phat_tile_sums(codes, scales, 64)
+    assert np.allclose(t, [[20.0, 8.0]])
+
+
+def test_accuracy_rows_and_rel_error():
+    import numpy as np
+    b = _bench()
+    small = synth.Workload("s", 1, 4, 1, 256, 256, 64, False, False, 0.0, 64, 1, (1,))
+    assert np.array_equal(b.accuracy_rows(small, 1), np.arange(1024))
+    big = synth.Workload("b", 8, 32, 8, 2048, 2048, 128, True, False, 0.0, 64, 1, (1,))
+    r = b.accuracy_rows(big, 4)
+    assert len(r) == 8 * 32 * 2048 // 16 and np.all(np.diff(r) > 0)
+    ref = np.array([[1.0, -2.0], [0.5, 0.25]])
+    got = np.array([[1.0, -1.0], [0.5, 0.0]])
+    emax, emean = b.rel_error(got, ref)
+    assert emax == 0.5 and emean == (0 + 0.5 + 0 + 0.5) / 4
+
+
+def test_cpu_info_reports_model_and_counts():
+    b = _bench()
+    info = b.cpu_info()
+    assert info["host_logical_cpus"] >= 1 and info["cpus_available"] >= 1
+    assert isinstance(info["cpu_model"], str) and info["cpu_model"]
