@@ -38,10 +38,29 @@ hifa4_status check_device() {
   return HIFA4_OK;
 }
 
+// Allocation ranges this thread has already found to be device memory.  A pointer
+// inside one of them needs no runtime query: the query takes a lock and a lookup in
+// the runtime's allocation map, and an attention call checks up to a dozen buffers,
+// most of them inside the same few allocations from one call to the next.  Host and
+// unregistered pointers never enter the cache, so they are rejected on every call.
+struct DevRange {
+  uintptr_t lo, hi;
+};
+constexpr int kRangeCache = 16;
+thread_local DevRange g_ranges[kRangeCache];
+thread_local int g_next_range = 0;
+
+bool cached_device(const void* p) {
+  const uintptr_t a = (uintptr_t)p;
+  for (int i = 0; i < kRangeCache; i++)
+    if (a >= g_ranges[i].lo && a < g_ranges[i].hi) return true;
+  return false;
+}
+
 // Device memory check for a caller buffer (NULL is accepted: callers check
 // presence separately).  Host and unregistered pointers are rejected.
 hifa4_status check_dev_ptr(const void* p, const char* name) {
-  if (!p) return HIFA4_OK;
+  if (!p || cached_device(p)) return HIFA4_OK;
   hipPointerAttribute_t attr;
   memset(&attr, 0, sizeof(attr));
   hipError_t e = hipPointerGetAttributes(&attr, p);
@@ -51,6 +70,14 @@ hifa4_status check_dev_ptr(const void* p, const char* name) {
   }
   if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
     return fail(HIFA4_EINVAL, "%s is not device memory", name);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && size > 0) {
+    g_ranges[g_next_range] = DevRange{(uintptr_t)base, (uintptr_t)base + size};
+    g_next_range = (g_next_range + 1) % kRangeCache;
+  } else {
+    (void)hipGetLastError();
+  }
   return HIFA4_OK;
 }
 

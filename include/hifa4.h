@@ -17,7 +17,10 @@
  * - Pointers named *_f16, codes, scales, s, inv_s, out and workspace are
  *   DEVICE pointers (hipMalloc'd or equivalent) on the current HIP device.
  *   The caller owns every buffer; the library allocates, frees and retains
- *   nothing, and keeps no global mutable state (calls are reentrant).
+ *   nothing.  Its only state is, per host thread, the address ranges of
+ *   allocations it has already checked to be device memory (a device pointer
+ *   inside one of them is accepted without another runtime query; freeing a
+ *   buffer and passing its old address again is the caller's error).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *   work is enqueued on it; only hifa4_calibrate_smooth synchronizes.
  * - Tensors are row-major.  Raw tensors are binary16, BHSD:
