@@ -50,7 +50,7 @@ class AttnArgs(ctypes.Structure):
 EXPORTS = (
     "hifa4_version", "hifa4_status_str", "hifa4_last_error", "hifa4_mx4_bytes",
     "hifa4_calibrate_smooth", "hifa4_quantize_qkv", "hifa4_attn_workspace_bytes",
-    "hifa4_attn_fwd", "hifa4_kv_append",
+    "hifa4_attn_fwd", "hifa4_attn_fwd_noalloc", "hifa4_kv_append",
 )
 
 
@@ -79,6 +79,9 @@ def load(path: str = LIB_PATH):
     lib.hifa4_attn_fwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci,
                                    ctypes.POINTER(AttnArgs), vp]
     lib.hifa4_attn_fwd.restype = ci
+    lib.hifa4_attn_fwd_noalloc.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci,
+                                           ctypes.POINTER(AttnArgs), vp]
+    lib.hifa4_attn_fwd_noalloc.restype = ci
     lib.hifa4_kv_append.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, ci, vp,
                                     vp, vp, vp, vp, vp, vp]
     lib.hifa4_kv_append.restype = ci
@@ -129,6 +132,13 @@ def hifa4_quantize_qkv(q, k, v, B, Hq, Hkv, N_q, N_kv, d, smooth, s, inv_s, q_co
 def hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args: AttnArgs, stream):
     _check(load().hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, int(causal), int(smooth), int(reorder),
                                  ctypes.byref(args), stream), "hifa4_attn_fwd")
+
+
+def hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args: AttnArgs,
+                           stream):
+    _check(load().hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, int(causal), int(smooth),
+                                         int(reorder), ctypes.byref(args), stream),
+           "hifa4_attn_fwd_noalloc")
 
 
 def hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos, rope_sin, rope_rows,
@@ -242,6 +252,19 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=workspace,
                      num_splits=num_splits, kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity)
     hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args, _stream(stream))
+    return out
+
+
+def attn_fwd_noalloc(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int,
+                     N_q: int, N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool,
+                     out, q_f16=None, s=None, num_splits: int = 1, kv_tile: int = 64,
+                     phat: Optional[MX4] = None, kv_capacity: int = 0, stream=None):
+    """attn_fwd through the entry point that allocates nothing: the caller passes `out`, and
+    the split-KV partial states use the library's static device scratch."""
+    args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=None, num_splits=num_splits,
+                     kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity)
+    hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args,
+                           _stream(stream))
     return out
 
 

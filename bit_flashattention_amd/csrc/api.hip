@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/hifa4.h"
@@ -87,11 +88,41 @@ hifa4_status hip_fail(hipError_t e, const char* what) {
 
 bool supported_d(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
+// Scratch of hifa4_attn_fwd_noalloc: the split-KV partial states (fp32 O, then fp32
+// (m, l) pairs) live in this array instead of a caller workspace.  Each device that
+// runs the library holds its own copy until the process ends.  Host code never uses
+// the array's name as an address: it takes the device address from
+// hipGetSymbolAddress once per device and passes that to the kernels.
+static __device__ __align__(256) unsigned char scratch[HIFA4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call on
+// that device), or an error status.
+hifa4_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HIFA4_EHIP, "attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HIFA4_EUNSUPPORTED, "attn_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(HIFA4_EHIP, "attn_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HIFA4_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int hifa4_version(void) { return 101; }
+int hifa4_version(void) { return 102; }
 
 const char* hifa4_status_str(hifa4_status s) {
   switch (s) {
@@ -206,9 +237,13 @@ hifa4_status hifa4_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t N_q, int6
   return ok();
 }
 
-hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
-                            int64_t d, int causal, int smooth, int reorder,
-                            const hifa4_attn_args* a, void* stream) {
+}  // extern "C"
+
+// The attention call with its split-KV workspace given explicitly: the caller's
+// (hifa4_attn_fwd) or the static scratch (hifa4_attn_fwd_noalloc, scratch = true).
+static hifa4_status attn_fwd_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                                  int64_t d, int causal, int smooth, int reorder,
+                                  const hifa4_attn_args* a, bool use_scratch, void* stream) {
   if (!a) return fail(HIFA4_EINVAL, "attn: NULL args");
   if (B < 0 || N_q < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
     return fail(HIFA4_EINVAL, "attn: need B, N_q >= 0, Hq, Hkv > 0 and Hq %% Hkv == 0");
@@ -241,7 +276,8 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
       !aligned(a->v_scales, 16) ||
       (a->q_codes && (!aligned(a->q_codes, 16) || !aligned(a->q_scales, 8))) ||
       (a->q_f16 && !aligned(a->q_f16, 16)) || (a->s && !aligned(a->s, 16)) || !aligned(a->out_f16, 8) ||
-      (a->phat_codes && !aligned(a->phat_codes, 16)) || (a->workspace && !aligned(a->workspace, 16)))
+      (a->phat_codes && !aligned(a->phat_codes, 16)) ||
+      (!use_scratch && a->workspace && !aligned(a->workspace, 16)))
     return fail(HIFA4_EINVAL, "attn: misaligned buffer");
   const int64_t cap = a->kv_capacity ? a->kv_capacity : hifa4::pad_tokens(N_kv);
   if (cap < N_kv || cap % hifa4::kTokenPad != 0)
@@ -249,17 +285,27 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
                 (int)hifa4::kTokenPad);
   size_t need = 0;
   hifa4_attn_workspace_bytes(B, Hq, N_q, d, a->num_splits, &need);
+  if (use_scratch && need > (size_t)HIFA4_NOALLOC_SCRATCH_BYTES)
+    return fail(HIFA4_ENOSPACE,
+                "attn_noalloc: the split-KV partial states need %zu bytes, more than the %zu-byte "
+                "static scratch (use fewer splits, or hifa4_attn_fwd with a workspace)",
+                need, (size_t)HIFA4_NOALLOC_SCRATCH_BYTES);
   hifa4_status st = check_device();
   if (st) return st;
   const void* ptrs[] = {a->q_codes, a->q_scales, a->q_f16, a->s, a->k_codes, a->k_scales,
-                        a->v_codes, a->v_scales, a->out_f16, a->workspace, a->phat_codes,
-                        a->phat_scales};
+                        a->v_codes, a->v_scales, a->out_f16,
+                        use_scratch ? nullptr : a->workspace, a->phat_codes, a->phat_scales};
   const char* names[] = {"q_codes", "q_scales", "q_f16", "s", "k_codes", "k_scales", "v_codes",
                          "v_scales", "out", "workspace", "phat_codes", "phat_scales"};
   for (int i = 0; i < 12; i++)
     if ((st = check_dev_ptr(ptrs[i], names[i]))) return st;
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+  void* ws = a->workspace;
+  if (use_scratch) {
+    ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws))) return st;
+  } else if (need > 0 && (!a->workspace || a->workspace_bytes < need)) {
     return fail(HIFA4_ENOSPACE, "attn: workspace needs %zu bytes", need);
+  }
 
   hifa4::AttnLaunch L;
   L.q_codes = a->q_codes;
@@ -273,8 +319,8 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   L.out = (uint16_t*)a->out_f16;
   L.phat_codes = a->phat_codes;
   L.phat_scales = a->phat_scales;
-  L.ws_o = (float*)a->workspace;
-  L.ws_ml = a->workspace ? (float*)a->workspace + B * Hq * N_q * a->num_splits * d : nullptr;
+  L.ws_o = (float*)ws;
+  L.ws_ml = ws ? (float*)ws + B * Hq * N_q * a->num_splits * d : nullptr;
   L.B = B;
   L.Hq = Hq;
   L.Hkv = Hkv;
@@ -296,6 +342,20 @@ hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int
   }
   if (e != hipSuccess) return hip_fail(e, "attn launch");
   return ok();
+}
+
+extern "C" {
+
+hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                            int64_t d, int causal, int smooth, int reorder,
+                            const hifa4_attn_args* a, void* stream) {
+  return attn_fwd_impl(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, a, false, stream);
+}
+
+hifa4_status hifa4_attn_fwd_noalloc(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
+                                    int64_t d, int causal, int smooth, int reorder,
+                                    const hifa4_attn_args* a, void* stream) {
+  return attn_fwd_impl(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, a, true, stream);
 }
 
 hifa4_status hifa4_kv_append(const void* k_new_f16, const void* v_new_f16, int64_t B,

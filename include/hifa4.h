@@ -17,7 +17,8 @@
  * - Pointers named *_f16, codes, scales, s, inv_s, out and workspace are
  *   DEVICE pointers (hipMalloc'd or equivalent) on the current HIP device.
  *   The caller owns every buffer; the library allocates, frees and retains
- *   nothing.  Its only state is, per host thread, the address ranges of
+ *   nothing.  Its only state is the static device scratch of
+ *   hifa4_attn_fwd_noalloc (below) and, per host thread, the address ranges of
  *   allocations it has already checked to be device memory (a device pointer
  *   inside one of them is accepted without another runtime query; freeing a
  *   buffer and passing its old address again is the caller's error).
@@ -61,6 +62,8 @@ extern "C" {
 
 #define HIFA4_TOKEN_PAD 128
 #define HIFA4_MAX_NKV 32768 /* l <= 1.5 * N_kv must stay below binary16's 65504 */
+/* Size of the static device scratch of hifa4_attn_fwd_noalloc (16 MiB per device). */
+#define HIFA4_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum {
   HIFA4_OK = 0,
@@ -193,6 +196,24 @@ hifa4_status hifa4_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t N_q, int6
 hifa4_status hifa4_attn_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
                             int64_t d, int causal, int smooth, int reorder,
                             const hifa4_attn_args* args, void* stream);
+
+/*
+ * The same operation as hifa4_attn_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  Arguments, layouts and results are those of hifa4_attn_fwd, except that
+ * args->workspace and args->workspace_bytes are ignored: the split-KV partial states
+ * (the only scratch any kernel here uses) go to a static device array of
+ * HIFA4_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it runs on
+ * until the process ends.  Calls needing more than that (hifa4_attn_workspace_bytes
+ * above the limit) return HIFA4_ENOSPACE on the host, before any device work.  The call
+ * allocates and frees nothing.  Every call on one device shares that device's array
+ * and each call writes every partial state it later reads, so nothing needs clearing
+ * between calls; but calls that overlap in time on one device (different streams, or
+ * host threads) race on the array and must be serialized by the caller.
+ */
+hifa4_status hifa4_attn_fwd_noalloc(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q,
+                                    int64_t N_kv, int64_t d, int causal, int smooth,
+                                    int reorder, const hifa4_attn_args* args, void* stream);
 
 /*
  * Decode-time KV-cache append (HiFA4 Abstract: Smooth-QK rescales K after

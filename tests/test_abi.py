@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(hf):
 
 def test_status_strings_and_version(hf):
     lib = hf.load()
-    assert lib.hifa4_version() == 101
+    assert lib.hifa4_version() == 102
     for s in range(6):
         assert lib.hifa4_status_str(s)
     assert b"unknown" in lib.hifa4_status_str(99)
@@ -206,3 +206,20 @@ def test_kv_append_empty_is_noop(hf):
     with pytest.raises(hf.HiFA4Error) as e:
         _append(hf, v=None, vc=None, vs=None, stage=None)
     assert e.value.status in (hf.ENODEV, hf.EINVAL)  # valid sizes: fails only at the device check
+
+
+def test_attn_noalloc_rejects_oversized_scratch_on_host(hf):
+    """The no-allocation entry point validates like hifa4_attn_fwd, and a split-KV call whose
+    partial states exceed the static scratch (B=64, Hq=32, one query, 16 splits at d=128:
+    64*32*16*130*4 = 17,039,360 bytes > 16 MiB) fails with ENOSPACE before any device work."""
+    a = _args(hf, num_splits=16)
+    need = hf.hifa4_attn_workspace_bytes(64, 32, 1, 128, 16)
+    assert need == 17_039_360 > (16 << 20)
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_attn_fwd_noalloc(64, 32, 8, 1, 8192, 128, 0, 0, 1, a, None)
+    assert e.value.status == hf.ENOSPACE
+    assert b"static scratch" in hf.load().hifa4_last_error()
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_attn_fwd_noalloc(1, 8, 2, 64, 256, 96, 0, 0, 1, _args(hf), None)
+    assert e.value.status == hf.EUNSUPPORTED
+    hf.hifa4_attn_fwd_noalloc(1, 8, 2, 0, 256, 128, 0, 0, 1, _args(hf), None)  # empty: no-op
