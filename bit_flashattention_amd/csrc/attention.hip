@@ -407,17 +407,23 @@ struct Stage {
   static_assert((N_KC + N_VC) % 4 == 0 && SCU % 4 == 0 && SCU / 4 <= 64, "even split over 4 waves");
 };
 
-// Tile copies are direct global -> LDS transfers (global_load_lds_dwordx4):
+// Tile copies are direct buffer -> LDS transfers (buffer_load_dwordx4 ... lds):
 // one instruction moves 16 bytes per lane into LDS lane after lane, so 64
 // lanes fill one 1 KB MFMA operand piece of the stage.  Each of the 4
 // wavefronts copies CPW code pieces and a quarter of the scale bytes (its
-// first SCU/4 lanes).  Sources are for the tile at key 0; the tile at kb0
-// adds kb0 * D/2 bytes to a code source (K_hat rows and 64-token V_hat tiles
-// alike) and kb0 * D/32 to a scale source.
+// first SCU/4 lanes).  A piece is a buffer resource on its source tensor (the
+// KV head's codes or scales, wave-uniform, in scalar registers) plus a per-lane
+// byte offset for the tile at key 0; the tile at kb0 adds kb0 * D/2 bytes (code
+// pieces: K_hat rows and 64-token V_hat tiles alike) or kb0 * D/32 (scale
+// pieces) through the instruction's scalar offset, so a copy takes no vector
+// instruction for its address.
 template <int D, int KT>
 struct DmaPlan {
-  // piece j: source base (wave-uniform) + per-lane 32-bit offset; the last one is the scale unit
-  const uint8_t* base[Stage<D, KT>::CPW + 1];
+  const uint8_t* kc;  // K_hat codes of the KV head
+  const uint8_t* vc;  // V_hat codes
+  const uint8_t* sc;  // this wave's scale tensor (K_hat's or V_hat's)
+  uint32_t code_bytes, scale_bytes;
+  int nk;  // pieces j < nk are K_hat codes, the rest V_hat (wave-uniform)
   uint32_t off[Stage<D, KT>::CPW + 1];
   int dst[Stage<D, KT>::CPW + 1];  // LDS offset in the stage (wave-uniform)
 };
@@ -431,32 +437,52 @@ struct KvBases {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// A raw buffer resource on a wave-uniform pointer (its two halves read from the
+// first lane, so the resource lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint8_t* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* q = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte-per-lane copy from base + voff + soff into LDS at `lds` (lane after lane).
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* base, uint32_t bytes, uint8_t* lds, uint32_t voff,
+                                              int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(uniform_rsrc(base, bytes), (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
 template <int D, int KT>
-__device__ __forceinline__ void make_dma_plan(const KvBases& kv, DmaPlan<D, KT>& pl) {
+__device__ __forceinline__ void make_dma_plan(const KvBases& kv, uint32_t code_bytes, uint32_t scale_bytes,
+                                              DmaPlan<D, KT>& pl) {
   using S = Stage<D, KT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
+  pl.kc = kv.kc;
+  pl.vc = kv.vc;
+  pl.code_bytes = code_bytes;
+  pl.scale_bytes = scale_bytes;
+  pl.nk = (S::N_KC - wave + 3) / 4;  // pieces i = wave + 4 j below N_KC
 #pragma unroll
   for (int j = 0; j < S::CPW; j++) {
     const int i = wave + 4 * j;
     if (i < S::N_KC) {
       const int b = i / S::KS, sk = i % S::KS;
-      pl.base[j] = kv.kc + 32 * b * (D / 2) + 2 * sk * 16;
-      pl.off[j] = (uint32_t)(l32 * (D / 2) + hf * 16);
+      pl.off[j] = (uint32_t)(32 * b * (D / 2) + 2 * sk * 16 + l32 * (D / 2) + hf * 16);
       pl.dst[j] = S::KC_OFF + i * 1024;
     } else {
       const int jj = i - S::N_KC, u = jj / S::CT, ct = jj % S::CT;
-      pl.base[j] = kv.vc + (u * D + 32 * ct) * 32;
-      pl.off[j] = (uint32_t)(l32 * 32 + 16 * hf);
+      pl.off[j] = (uint32_t)((u * D + 32 * ct) * 32 + l32 * 32 + 16 * hf);
       pl.dst[j] = S::VC_OFF + jj * 1024;
     }
   }
   // scale units: waves 0-1 copy K_hat's, waves 2-3 V_hat's (KSC_BYTES = VSC_BYTES)
   constexpr int KU = S::KSC_BYTES / 16, PU = S::SCU / 4;
   static_assert(KU == 2 * PU, "each wave's scale units come from one tensor");
-  pl.base[S::CPW] = wave < 2 ? kv.ks + wave * PU * 16 : kv.vs + (wave - 2) * PU * 16;
-  pl.off[S::CPW] = (uint32_t)(lane * 16);
+  pl.sc = wave < 2 ? kv.ks : kv.vs;
+  pl.off[S::CPW] = (uint32_t)((wave < 2 ? wave : wave - 2) * PU * 16 + lane * 16);
   pl.dst[S::CPW] = S::KSC_OFF + wave * PU * 16;
 }
 
@@ -468,12 +494,9 @@ __device__ __forceinline__ void dma_tile(const DmaPlan<D, KT>& pl, int kb0, uint
   using S = Stage<D, KT>;
 #pragma unroll
   for (int j = 0; j < S::CPW; j++)
-    __builtin_amdgcn_global_load_lds((const void*)(pl.base[j] + (int64_t)kb0 * (D / 2) + pl.off[j]),
-                                     (lds_ptr_t)(stage + pl.dst[j]), 16, 0, 0);
+    copy16_to_lds(j < pl.nk ? pl.kc : pl.vc, pl.code_bytes, stage + pl.dst[j], pl.off[j], kb0 * (D / 2));
   if ((threadIdx.x & 63) < S::SCU / 4)
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(pl.base[S::CPW] + (int64_t)kb0 * (D / 32) + pl.off[S::CPW]),
-        (lds_ptr_t)(stage + pl.dst[S::CPW]), 16, 0, 0);
+    copy16_to_lds(pl.sc, pl.scale_bytes, stage + pl.dst[S::CPW], pl.off[S::CPW], kb0 * (D / 32));
 }
 
 // V_hat operands read from an LDS stage.
@@ -561,7 +584,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   // runs under tile t's compute; the barrier that ends tile t waits for it.
   // The first tile's copy is issued before the query work so that it overlaps.
   DmaPlan<D, KT> plan;
-  make_dma_plan<D, KT>(kv, plan);
+  make_dma_plan<D, KT>(kv, (uint32_t)(p.Npad_kv * (D / 2)), (uint32_t)(p.Npad_kv * (D / 32)), plan);
   dma_tile<D, KT>(plan, 0, st0);
 
   // Q_hat rows of this wave: B operand of S^T, resident for the whole loop.
