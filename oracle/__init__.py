@@ -67,7 +67,7 @@ class AttnParams(ctypes.Structure):
         ("sum_p", ctypes.c_void_p), ("sum_phat", ctypes.c_void_p),
         ("m_out", ctypes.c_void_p), ("l_out", ctypes.c_void_p),
         ("rows", ctypes.c_void_p), ("n_rows", ctypes.c_int64),
-        ("threads", ctypes.c_int),
+        ("threads", ctypes.c_int), ("scale_rule", ctypes.c_int),
     ]
 
 
@@ -86,12 +86,14 @@ def _load():
         lib.orc_e2m1_encode.restype = ctypes.c_int
         lib.orc_e2m1_decode.argtypes = [ctypes.c_int]
         lib.orc_e2m1_decode.restype = ctypes.c_float
-        lib.orc_mx_exponent.argtypes = [vp, ctypes.c_int]
+        lib.orc_mx_exponent.argtypes = [vp, ctypes.c_int, ctypes.c_int]
         lib.orc_mx_exponent.restype = ctypes.c_int
-        lib.orc_mx_block.argtypes = [vp, ctypes.c_int, vp, vp]
+        lib.orc_mx_block.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int]
+        lib.orc_phat_exponent.argtypes = [ctypes.c_float, ctypes.c_int]
+        lib.orc_phat_exponent.restype = ctypes.c_int
         lib.orc_calibrate.argtypes = [vp, vp, i64, i64, i64, i64, i64, dbl, vp, vp]
-        lib.orc_quantize_rows.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
-        lib.orc_quantize_v.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp]
+        lib.orc_quantize_rows.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.c_int]
+        lib.orc_quantize_v.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, ctypes.c_int]
         lib.orc_attn.argtypes = [ctypes.POINTER(AttnParams)]
         lib.orc_attn.restype = ctypes.c_int
         lib.orc_attn_exact.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
@@ -160,18 +162,28 @@ def e2m1_decode(code: int) -> float:
     return _load().orc_e2m1_decode(int(code))
 
 
-def mx_block(x) -> tuple:
+# block-exponent rules: the OCP MX rule (saturates blocks whose amax * 2^-e lands in
+# [6, 8)) and the no-clipping rule (smallest e with amax * 2^-e <= 6)
+RULE_OCP, RULE_NOCLIP = 0, 1
+
+
+def mx_block(x, rule: int = RULE_OCP) -> tuple:
     """Quantize <= 32 values: (codes uint8[n], scale byte)."""
     xa = np.ascontiguousarray(x, dtype=np.float32)
     codes = np.zeros(len(xa), dtype=np.uint8)
     sc = np.zeros(1, dtype=np.uint8)
-    _load().orc_mx_block(_p(xa), len(xa), _p(codes), _p(sc))
+    _load().orc_mx_block(_p(xa), len(xa), _p(codes), _p(sc), int(rule))
     return codes, int(sc[0])
 
 
-def mx_exponent(x) -> int:
+def mx_exponent(x, rule: int = RULE_OCP) -> int:
     xa = np.ascontiguousarray(x, dtype=np.float32)
-    return _load().orc_mx_exponent(_p(xa), len(xa))
+    return _load().orc_mx_exponent(_p(xa), len(xa), int(rule))
+
+
+def phat_exponent(tmax: float, rule: int = RULE_OCP) -> int:
+    """Block exponent of P_hat from the block's largest t (P = 2^t)."""
+    return _load().orc_phat_exponent(float(tmax), int(rule))
 
 
 # ---- tensors --------------------------------------------------------------
@@ -186,24 +198,26 @@ def calibrate(q_cal: np.ndarray, k_cal: np.ndarray, alpha: float):
     return s, inv
 
 
-def quantize_rows(x: np.ndarray, Hkv: int, mult: Optional[np.ndarray] = None):
+def quantize_rows(x: np.ndarray, Hkv: int, mult: Optional[np.ndarray] = None,
+                  rule: int = RULE_OCP):
     """[B][H][N][d] f16 -> (codes [B][H][Npad][d/2], scales [B][H][Npad][d/32])."""
     B, H, N, d = x.shape
     Np = padded(N)
     codes = np.zeros((B, H, Np, d // 2), dtype=np.uint8)
     scales = np.zeros((B, H, Np, d // 32), dtype=np.uint8)
     m = None if mult is None else np.ascontiguousarray(mult, dtype=np.float32)
-    _load().orc_quantize_rows(_p(_f16bits(x)), B, H, Hkv, N, Np, d, _p(m), _p(codes), _p(scales))
+    _load().orc_quantize_rows(_p(_f16bits(x)), B, H, Hkv, N, Np, d, _p(m), _p(codes), _p(scales),
+                              int(rule))
     return codes, scales
 
 
-def quantize_v(v: np.ndarray):
+def quantize_v(v: np.ndarray, rule: int = RULE_OCP):
     """[B][H][N][d] f16 -> (codes [B][H][d][Npad/2], scales [B][H][d][Npad/32])."""
     B, H, N, d = v.shape
     Np = padded(N)
     codes = np.zeros((B, H, d, Np // 2), dtype=np.uint8)
     scales = np.zeros((B, H, d, Np // 32), dtype=np.uint8)
-    _load().orc_quantize_v(_p(_f16bits(v)), B, H, N, Np, d, _p(codes), _p(scales))
+    _load().orc_quantize_v(_p(_f16bits(v)), B, H, N, Np, d, _p(codes), _p(scales), int(rule))
     return codes, scales
 
 
@@ -225,7 +239,8 @@ def rope_f16(x: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray, pos0: int = 0)
 def attn(B, Hq, Hkv, N_q, N_kv, d, *, causal, reorder, kv_tile=64, num_splits=1,
          q4=None, k4=None, v4=None, q_f32=None, k_f32=None, v_f32=None, state_fp16=True,
          rows: Optional[np.ndarray] = None, want_phat=False, want_sums=False, want_f32=False,
-         want_state=False, threads: int = 0, npad_kv: Optional[int] = None) -> dict:
+         want_state=False, threads: int = 0, npad_kv: Optional[int] = None,
+         scale_rule: int = RULE_OCP) -> dict:
     """Run the oracle forward.  q4/k4/v4 are (codes, scales) pairs (quantized mode) or
     q_f32/k_f32/v_f32 real tensors (quant-off mode).  Outputs are indexed by the
     position in `rows` (flat ids (b*Hq + h)*N_q + i) or by the flat id when rows is None."""
@@ -269,6 +284,7 @@ def attn(B, Hq, Hkv, N_q, N_kv, d, *, causal, reorder, kv_tile=64, num_splits=1,
         keep.append(r)
         P.rows, P.n_rows = _p(r), len(r)
     P.threads = threads if threads > 0 else cpu_share()
+    P.scale_rule = int(scale_rule)
     rc = _load().orc_attn(ctypes.byref(P))
     if rc != 0:
         raise ValueError(f"orc_attn failed with {rc}")

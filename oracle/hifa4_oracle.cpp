@@ -97,21 +97,44 @@ int e2m1_rne(double x) {
 
 double e2m1_value(int code) { return (code & 8) ? -kE2M1[code & 7] : kE2M1[code & 7]; }
 
-// MX block exponent from the block's largest magnitude: clamp(floor(log2 a) - 2, -127, 127).
-// emax of E2M1 is 2 (its largest value 6 = 1.5 * 2^2).
-int mx_exponent_from_amax(double amax) {
+// MX block exponent from the block's largest magnitude a, clamped to [-127, 127].
+// rule 0 (the OCP MX rule): floor(log2 a) - 2, where 2 is the emax of E2M1 (its
+//   largest value 6 = 1.5 * 2^2); a block whose a * 2^-e lands in [6, 8) saturates.
+// rule 1 (no clipping): the smallest e with a * 2^-e <= 6, so nothing saturates.
+int mx_exponent_from_amax(double amax, int rule) {
   if (!(amax > 0.0)) return -127;
   int ex;
   std::frexp(amax, &ex);  // amax = fr * 2^ex, fr in [0.5, 1): floor(log2 amax) = ex - 1
-  return std::min(127, std::max(-127, (ex - 1) - 2));
+  int e = (ex - 1) - 2;
+  if (rule == 1 && std::ldexp(amax, -e) > 6.0) e += 1;  // a * 2^-e in [4, 8): one step up
+  return std::min(127, std::max(-127, e));
 }
 
-void mx_block(const float* x, int n, uint8_t* codes, uint8_t* scale) {
+void mx_block(const float* x, int n, uint8_t* codes, uint8_t* scale, int rule) {
   double amax = 0.0;
   for (int i = 0; i < n; i++) amax = std::max(amax, std::fabs((double)x[i]));
-  const int e = mx_exponent_from_amax(amax);
+  const int e = mx_exponent_from_amax(amax, rule);
   for (int i = 0; i < n; i++) codes[i] = (uint8_t)e2m1_rne(std::ldexp((double)x[i], -e));
   *scale = (uint8_t)(e + 127);
+}
+
+// Block exponent of P_hat from the largest t = S c - m of the block's valid keys
+// (P = 2^t), in the log domain so that it does not depend on the rounding of 2^t:
+// rule 0: floor(t_max) - 2 (the OCP rule applied to 2^t_max);
+// rule 1: the smallest e with 2^(t_max - e) <= 6 = 1.5 * 2^2, i.e.
+//         e = ceil(t_max - log2(3/2)) - 2, the difference taken as one fp32
+//         subtraction with log2(3/2) rounded to fp32.
+// Both clamped to [-127, 127].
+int phat_exponent(float tmax, int rule) {
+  int e;
+  if (rule == 1) {
+    const float lam = (float)std::log2(1.5);
+    const float u = tmax - lam;
+    e = (int)std::ceil(std::max(u, -200.0f)) - 2;
+  } else {
+    e = (int)std::floor(std::max(tmax, -200.0f)) - 2;
+  }
+  return std::min(127, std::max(-127, e));
 }
 
 inline void put_nibble(uint8_t* row, int64_t idx, int code) {
@@ -181,15 +204,17 @@ float orc_score(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* 
   return score_f32(a.data(), b.data(), d);
 }
 
-int orc_mx_exponent(const float* x, int n) {
+int orc_mx_exponent(const float* x, int n, int rule) {
   double amax = 0.0;
   for (int i = 0; i < n; i++) amax = std::max(amax, std::fabs((double)x[i]));
-  return mx_exponent_from_amax(amax);
+  return mx_exponent_from_amax(amax, rule);
 }
 
-void orc_mx_block(const float* x, int n, uint8_t* codes, uint8_t* scale) {
-  mx_block(x, n, codes, scale);
+void orc_mx_block(const float* x, int n, uint8_t* codes, uint8_t* scale, int rule) {
+  mx_block(x, n, codes, scale, rule);
 }
+
+int orc_phat_exponent(float tmax, int rule) { return phat_exponent(tmax, rule); }
 
 // Smooth-QK calibration (HiFA4 Abstract: a calibration-static per-channel
 // equivalent rescale of Q and K after RoPE).  The formula is not on the page;
@@ -223,7 +248,7 @@ void orc_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64_t B, int6
 // x = fp32(x_f16 * mult_j), one MX block per 32 consecutive channels.
 void orc_quantize_rows(const uint16_t* x, int64_t B, int64_t H, int64_t Hkv, int64_t N,
                        int64_t Npad, int64_t d, const float* mult, uint8_t* codes,
-                       uint8_t* scales) {
+                       uint8_t* scales, int rule) {
   const int64_t G = (Hkv > 0 && H >= Hkv) ? H / Hkv : 1;
   std::vector<float> blk(32);
   std::vector<uint8_t> c(32);
@@ -246,7 +271,7 @@ void orc_quantize_rows(const uint16_t* x, int64_t B, int64_t H, int64_t Hkv, int
             if (mult) v = v * mult[g * d + j];
             blk[i] = v;
           }
-          mx_block(blk.data(), 32, c.data(), &srow[blkno]);
+          mx_block(blk.data(), 32, c.data(), &srow[blkno], rule);
           for (int i = 0; i < 32; i++) put_nibble(crow, blkno * 32 + i, c[i]);
         }
       }
@@ -256,7 +281,7 @@ void orc_quantize_rows(const uint16_t* x, int64_t B, int64_t H, int64_t Hkv, int
 // V quantization along tokens: one MX block per 32 consecutive token positions
 // [32*beta, 32*beta + 32) of one channel; positions >= N count as 0.
 void orc_quantize_v(const uint16_t* v, int64_t B, int64_t H, int64_t N, int64_t Npad, int64_t d,
-                    uint8_t* codes, uint8_t* scales) {
+                    uint8_t* codes, uint8_t* scales, int rule) {
   std::vector<float> blk(32);
   std::vector<uint8_t> c(32);
   for (int64_t b = 0; b < B; b++)
@@ -269,7 +294,7 @@ void orc_quantize_v(const uint16_t* v, int64_t B, int64_t H, int64_t N, int64_t 
             const int64_t n = beta * 32 + i;
             blk[i] = (n < N) ? f16_to_f32(v[((b * H + h) * N + n) * d + j]) : 0.0f;
           }
-          mx_block(blk.data(), 32, c.data(), &srow[beta]);
+          mx_block(blk.data(), 32, c.data(), &srow[beta], rule);
           for (int i = 0; i < 32; i++) put_nibble(crow, beta * 32 + i, c[i]);
         }
       }
@@ -451,7 +476,7 @@ void run_row(const RowCtx& ctx, int64_t row, int64_t oi, UnitScratch& u) {
         if (v1 > blk0) {
           float tmax = NEG_INF;
           for (int64_t j = blk0; j < v1; j++) tmax = std::max(tmax, t[j - tB]);
-          e = std::min(127, std::max(-127, (int)std::floor(tmax) - 2));
+          e = phat_exponent(tmax, p->scale_rule);
         }
         for (int64_t j = blk0; j < blk1; j++) {
           const int64_t jj = j - tB;

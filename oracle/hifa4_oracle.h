@@ -50,10 +50,14 @@ float orc_score(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* 
 /* E2M1 element: RNE to {0,.5,1,1.5,2,3,4,6}, saturating at 6, sign kept. */
 int orc_e2m1_encode(float x);
 float orc_e2m1_decode(int code);
-/* Block exponent e = clamp(floor(log2 max|x|) - 2, -127, 127); all-zero -> -127. */
-int orc_mx_exponent(const float* x, int n);
+/* Block exponent, clamped to [-127, 127], all-zero block -> -127.  rule 0 (OCP MX):
+ * floor(log2 max|x|) - 2; rule 1 (no clipping): the smallest e with max|x| * 2^-e <= 6. */
+int orc_mx_exponent(const float* x, int n, int rule);
 /* Quantize n (<= 32) values into one MX block: codes[i] in 0..15, *scale = e + 127. */
-void orc_mx_block(const float* x, int n, uint8_t* codes, uint8_t* scale);
+void orc_mx_block(const float* x, int n, uint8_t* codes, uint8_t* scale, int rule);
+/* Block exponent of P_hat from the block's largest t (P = 2^t): rule 0: floor(t_max) - 2;
+ * rule 1: ceil(fp32(t_max - fp32(log2 1.5))) - 2; clamped to [-127, 127]. */
+int orc_phat_exponent(float tmax, int rule);
 
 /* Smooth-QK calibration: s[g][j] = kmax^alpha / qmax^(1-alpha), inv_s = 1/s (fp32). */
 void orc_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64_t B, int64_t Hq,
@@ -62,13 +66,14 @@ void orc_calibrate(const uint16_t* q_cal, const uint16_t* k_cal, int64_t B, int6
 /* Row-wise (along d) quantization of Q or K, optional per-(KV head, channel)
  * multiplier mult[Hkv][d] applied as fp32(x * mult) (Q uses s, K uses inv_s).
  * H is the tensor's own head count; head h reads mult row h / (H / Hkv).
- * Padding rows N..Npad-1 are written as zero codes and scale byte 0. */
+ * Padding rows N..Npad-1 are written as zero codes and scale byte 0.  rule: the
+ * block-exponent rule of orc_mx_exponent. */
 void orc_quantize_rows(const uint16_t* x, int64_t B, int64_t H, int64_t Hkv, int64_t N,
                        int64_t Npad, int64_t d, const float* mult, uint8_t* codes,
-                       uint8_t* scales);
+                       uint8_t* scales, int rule);
 /* Token-wise (32 tokens per block) quantization of V into [B][H][d][Npad/2]. */
 void orc_quantize_v(const uint16_t* v, int64_t B, int64_t H, int64_t N, int64_t Npad, int64_t d,
-                    uint8_t* codes, uint8_t* scales);
+                    uint8_t* codes, uint8_t* scales, int rule);
 
 /* RoPE (rotate-half: channel j < d/2 pairs with j + d/2) of binary16 rows
  * x [B][H][N][d] at positions pos0 .. pos0+N-1, tables cos/sin [n_rope][d/2]
@@ -100,6 +105,7 @@ typedef struct {
   const int64_t* rows;      /* optional list of flat row ids (b*Hq + h)*N_q + i; NULL = all */
   int64_t n_rows;
   int threads;
+  int scale_rule;           /* P_hat block exponent: 0 OCP, 1 no clipping (orc_phat_exponent) */
 } orc_attn_params;
 
 /* Returns 0 on success, negative on bad arguments. */

@@ -77,9 +77,10 @@ def e2m1_rne_value(x: float) -> float:
     return float(E2M1[k])
 
 
-def one_tile_state(qv, kv, vv, keys, c, reorder):
+def one_tile_state(qv, kv, vv, keys, c, reorder, rule=0):
     """State (m, l, O) of one row after the single tile of `keys` (valid keys only), from the
-    empty state."""
+    empty state.  rule 1 takes P_hat's block exponent as the smallest e with
+    2^(t_max - e) <= 6 = 2^(2 + log2 1.5), from one fp32 subtraction t_max - fp32(log2 1.5)."""
     if len(keys) == 0:
         return np.float32(-np.inf), np.float32(0.0), np.zeros(vv.shape[0], np.float32)
     S = [f32_round(sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qv, kv[j])),
@@ -93,7 +94,12 @@ def one_tile_state(qv, kv, vv, keys, c, reorder):
     for b0 in range(0, len(keys), 32):
         # keys of a tile start on a 32-key boundary, so list blocks are the MX blocks
         blk = range(b0, min(b0 + 32, len(keys)))
-        e = max(-127, min(127, int(np.floor(max(t[i] for i in blk))) - 2))
+        tmax = max(t[i] for i in blk)
+        if rule == 1:
+            u = np.float32(tmax - np.float32(np.log2(1.5)))
+            e = max(-127, min(127, int(np.ceil(u)) - 2))
+        else:
+            e = max(-127, min(127, int(np.floor(tmax)) - 2))
         for i in blk:
             Ph[i] = e2m1_rne_value(float(P[i]) * 2.0 ** -e) * 2.0 ** e
     rs = 0.0
@@ -120,7 +126,7 @@ def merge(states, round_L=True):
     return np.float16((A / lf).astype(np.float32))
 
 
-def split_reference(w, q4, k4, v4, kv_tile, chunk_tiles, reorder, round_L=True):
+def split_reference(w, q4, k4, v4, kv_tile, chunk_tiles, reorder, round_L=True, rule=0):
     """Rows of a single-head workload through chunks of `chunk_tiles` tiles each, where each
     chunk must be one tile (the closed form above)."""
     assert chunk_tiles == 1
@@ -136,7 +142,7 @@ def split_reference(w, q4, k4, v4, kv_tile, chunk_tiles, reorder, round_L=True):
         states = []
         for t in range(T):
             keys = [j for j in range(t * kv_tile, min((t + 1) * kv_tile, w.N_kv)) if j <= last]
-            states.append(one_tile_state(qd[i], kd, vd, keys, c, reorder))
+            states.append(one_tile_state(qd[i], kd, vd, keys, c, reorder, rule))
         out[i] = merge(states, round_L)
     return out
 
@@ -158,6 +164,25 @@ def test_split_merge_bitwise_one_tile_chunks(small, reorder, causal):
     got = oracle.attn(1, 1, 1, w.N_q, w.N_kv, w.d, causal=causal, reorder=reorder, kv_tile=64,
                       num_splits=T, q4=q4, k4=k4, v4=v4)["out"]
     assert np.array_equal(got.reshape(w.N_q, w.d), ref.view(np.uint16))
+
+
+def test_split_merge_bitwise_noclip_rule():
+    """The same closed form with every block exponent (Q, K, V and P_hat) from the
+    no-clipping rule, against the oracle run with that rule; and the rule matters here: the
+    default rule gives different bits on these inputs."""
+    w = synth.qwen3_8b(B=1, Hq=1, Hkv=1, N=6, N_kv=200, d=64, n_cal=32)
+    s, inv = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    q4 = oracle.quantize_rows(w.q, 1, s, oracle.RULE_NOCLIP)
+    k4 = oracle.quantize_rows(w.k, 1, inv, oracle.RULE_NOCLIP)
+    v4 = oracle.quantize_v(w.v, oracle.RULE_NOCLIP)
+    w.causal = False
+    ref = split_reference(w, q4, k4, v4, 64, 1, 1, rule=1)
+    got = oracle.attn(1, 1, 1, w.N_q, w.N_kv, w.d, causal=False, reorder=1, kv_tile=64,
+                      num_splits=4, q4=q4, k4=k4, v4=v4, scale_rule=1)["out"]
+    assert np.array_equal(got.reshape(w.N_q, w.d), ref.view(np.uint16))
+    other = oracle.attn(1, 1, 1, w.N_q, w.N_kv, w.d, causal=False, reorder=1, kv_tile=64,
+                        num_splits=4, q4=q4, k4=k4, v4=v4, scale_rule=0)["out"]
+    assert not np.array_equal(got, other)
 
 
 def test_split_merge_pin_detects_mistakes(small):
