@@ -111,7 +111,8 @@ def launch_stats(fn, torch, n=100):
             "p90_ms": float(np.percentile(t, 90)), "launches": n}
 
 
-def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=False):
+def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=False,
+                scale_rule=0):
     """Time `steps` full steps, then `steps` attention launches alone.  A step runs the
     Smooth-QK + quantize pass over Q, K and V, then the attention kernel; with raw_q the
     quantize pass covers K and V only and the attention kernel smooths and quantizes the
@@ -127,11 +128,12 @@ def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=F
     def attn():
         hf.attn_fwd(q4a, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
                     causal=w.causal, smooth=w.smooth, reorder=reorder, out=st["out"],
-                    kv_tile=kv_tile, **qarg)
+                    kv_tile=kv_tile, scale_rule=scale_rule, **qarg)
 
     def step():
         hf.quantize_qkv(qin, st["k"], st["v"], Hkv=w.Hkv, smooth=w.smooth, s=st["s"],
-                        inv_s=st["inv"], out=(None if raw_q else q4, k4, v4))
+                        inv_s=st["inv"], out=(None if raw_q else q4, k4, v4),
+                        scale_rule=scale_rule)
         attn()
 
     device_warmup(step, torch)
@@ -365,21 +367,21 @@ def eps_bar_summary(eb, mw, workload):
                           "below": int(np.sum(eb < -0.2)), "above": int(np.sum(eb > 0.2))}}
 
 
-def eps_bar_gpu_dump(w, hf, torch, kv_tile=64):
+def eps_bar_gpu_dump(w, hf, torch, kv_tile=64, scale_rule=0):
     """GPU half of the epsilon-bar diagnostic: one P_hat-dumping launch of the whole workload
     (off the timed path); returns the dump (device tensors, [rows][Npad/2] codes and
     [rows][Npad/32] scale bytes)."""
     st = prepare_prefill(w, hf, torch)
     q4, k4, v4 = st["bufs"]
     hf.quantize_qkv(st["q"], st["k"], st["v"], Hkv=w.Hkv, smooth=w.smooth, s=st["s"],
-                    inv_s=st["inv"], out=st["bufs"])
+                    inv_s=st["inv"], out=st["bufs"], scale_rule=scale_rule)
     total = w.B * w.Hq * w.N_q
     npk = (w.N_kv + 127) // 128 * 128
     phat = hf.MX4(torch.zeros((total, npk // 2), dtype=torch.uint8, device="cuda"),
                   torch.zeros((total, npk // 32), dtype=torch.uint8, device="cuda"))
     hf.attn_fwd(q4, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
                 causal=w.causal, smooth=w.smooth, reorder=True, out=st["out"], kv_tile=kv_tile,
-                phat=phat)
+                phat=phat, scale_rule=scale_rule)
     torch.cuda.synchronize()
     codes, scales = phat.codes.cpu().numpy(), phat.scales.cpu().numpy()
     del st, phat
@@ -423,12 +425,12 @@ def cpu_leg(w, gpu_out, eps_inputs, acc_inputs, target_s=12.0, seed=777):
     import synth
     res = {}
 
-    def quant(wk):
+    def quant(wk, rule=0):
         s_ref = inv_ref = None
         if wk.smooth:
             s_ref, inv_ref = oracle.calibrate(wk.q_cal, wk.k_cal, wk.alpha)
-        return (oracle.quantize_rows(wk.q, wk.Hkv, s_ref), oracle.quantize_rows(wk.k, wk.Hkv, inv_ref),
-                oracle.quantize_v(wk.v))
+        return (oracle.quantize_rows(wk.q, wk.Hkv, s_ref, rule),
+                oracle.quantize_rows(wk.k, wk.Hkv, inv_ref, rule), oracle.quantize_v(wk.v, rule))
 
     rq, rk, rv = quant(w)
     threads = oracle.cpu_share()
@@ -460,7 +462,7 @@ def cpu_leg(w, gpu_out, eps_inputs, acc_inputs, target_s=12.0, seed=777):
     # error against fp64 exact attention, every workload
     acc = {}
     for name, wk, arows, outs, kw in acc_inputs:
-        q3, k3, v3 = quant(wk)
+        q3, k3, v3 = quant(wk, kw.get("scale_rule", 0))
         exact = oracle.attn_exact(wk.q, wk.k, wk.v, wk.causal, rows=arows, threads=threads)
         entry = {"rows": int(len(arows)), "rows_total": int(wk.B * wk.Hq * wk.N_q)}
         for reorder, gout in outs.items():
@@ -492,9 +494,9 @@ def cpu_leg(w, gpu_out, eps_inputs, acc_inputs, target_s=12.0, seed=777):
                         "kv_gbs": wk.kv_bytes / dt3 / 1e9}
     res["cpu_oracle_single_thread"] = single
 
-    if eps_inputs is not None:
-        we, codes, scales = eps_inputs
-        q2, k2, v2 = quant(we)
+    # eps_inputs: (label, workload, dumped P_hat codes, scales, block-exponent rule) per run
+    for label, we, codes, scales, rule in (eps_inputs or []):
+        q2, k2, v2 = quant(we, rule)
         heads = we.B * we.Hq
         chunk = 8  # heads per oracle call
         ebs, mws, dev_max = [], [], 0.0
@@ -503,7 +505,7 @@ def cpu_leg(w, gpu_out, eps_inputs, acc_inputs, target_s=12.0, seed=777):
             erows = np.arange(h0 * we.N_q, h1 * we.N_q, dtype=np.int64)
             r2 = oracle.attn(we.B, we.Hq, we.Hkv, we.N_q, we.N_kv, we.d, causal=we.causal,
                              reorder=1, kv_tile=64, q4=q2, k4=k2, v4=v2, rows=erows,
-                             want_sums=True, threads=threads)
+                             want_sums=True, threads=threads, scale_rule=rule)
             sp, sph = r2["sum_p"], r2["sum_phat"]
             T = sp.shape[1]
             gph = phat_tile_sums(codes[erows], scales[erows], 64)[:, :T]
@@ -515,9 +517,10 @@ def cpu_leg(w, gpu_out, eps_inputs, acc_inputs, target_s=12.0, seed=777):
             ebs.append(eb)
             mws.append(mw)
         eb, mw = np.concatenate(ebs), np.concatenate(mws)
-        res["eps_bar"] = eps_bar_summary(
-            eb, mw, f"{we.name}: all {heads} (b, h) heads, tiles of 64 rows x 64 keys")
-        res["eps_bar"]["gpu_dump_sum_phat_max_rel_dev"] = dev_max
+        res[label] = eps_bar_summary(
+            eb, mw, f"{we.name}: all {heads} (b, h) heads, tiles of 64 rows x 64 keys, "
+                    f"{'no-clipping' if rule else 'OCP'} block-exponent rule")
+        res[label]["gpu_dump_sum_phat_max_rel_dev"] = dev_max
     return res
 
 
@@ -682,8 +685,25 @@ def main():
             if not a.no_cpu:
                 acc_inputs.append((name, wx, xrows, xouts,
                                    dict(kv_tile=default_kv_tile(wx.d, wx.N_kv))))
-            if name.startswith("llama") and not a.no_cpu:
-                eps_inputs = (wx,) + eps_bar_gpu_dump(wx, hf, torch)
+            if name.startswith("llama"):
+                # the no-clipping block-exponent rule on the same batch (every 4-bit block)
+                nouts = {}
+                for reorder in (True, False):
+                    msn, attnn, stn = run_prefill(wx, hf, torch, a.steps, a.warmup,
+                                                  reorder=reorder, scale_rule=1)
+                    key = name + "_noclip" + ("" if reorder else "_reorder_off")
+                    extra[key] = {"ms_per_step": msn, "attn_ms": attnn,
+                                  "attn_tflops": wx.flops / (attnn * 1e-3) / 1e12}
+                    log(f"[bench] {key}: step {msn:.4f} ms, attention {attnn:.4f} ms")
+                    if not a.no_cpu:
+                        nouts[int(reorder)] = rows_to_host(stn["out"], xrows, wx.d, torch)
+                    del stn
+                if not a.no_cpu:
+                    acc_inputs.append((name + "_noclip", wx, xrows, nouts,
+                                       dict(kv_tile=default_kv_tile(wx.d, wx.N_kv), scale_rule=1)))
+                    eps_inputs = [("eps_bar", wx) + eps_bar_gpu_dump(wx, hf, torch) + (0,),
+                                  ("eps_bar_noclip", wx) + eps_bar_gpu_dump(wx, hf, torch,
+                                                                            scale_rule=1) + (1,)]
         wd = synth.decode()
         msd, attnd, std = run_decode(wd, hf, torch, a.steps, a.warmup)
         gbs = wd.kv_bytes / (attnd * 1e-3) / 1e9
@@ -750,10 +770,11 @@ def main():
                         f"{e['gpu_vs_oracle_max']:.1e}")
         for k, v in cl.get("cpu_oracle_single_thread", {}).items():
             log(f"[bench] cpu oracle, one thread, {k}: {v['seconds']:.2f} s")
-        if "eps_bar" in cl:
-            eb = cl["eps_bar"]
-            log(f"[bench] eps_bar over {eb['tiles']} tiles: median {eb['median']:.4f}, "
-                f"{100 * eb['fraction_negative']:.1f} % negative")
+        for key in ("eps_bar", "eps_bar_noclip"):
+            if key in cl:
+                eb = cl[key]
+                log(f"[bench] {key} over {eb['tiles']} tiles: median {eb['median']:.4f}, "
+                    f"{100 * eb['fraction_negative']:.1f} % negative")
         extra.update(cl)
     if extra:
         result["extra"] = extra

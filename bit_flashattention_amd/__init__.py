@@ -22,6 +22,8 @@ TOKEN_PAD = 128
 MAX_NKV = 32768
 
 OK, EINVAL, EUNSUPPORTED, ENODEV, EHIP, ENOSPACE = range(6)
+# block-exponent rules (hifa4.h): the OCP MX rule, and the smallest exponent that clips nothing
+SCALE_OCP, SCALE_NOCLIP = 0, 1
 
 _lib = None
 
@@ -43,7 +45,7 @@ class AttnArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("kv_tile", ctypes.c_int), ("num_splits", ctypes.c_int),
         ("phat_codes", ctypes.c_void_p), ("phat_scales", ctypes.c_void_p),
-        ("kv_capacity", ctypes.c_int64),
+        ("kv_capacity", ctypes.c_int64), ("scale_rule", ctypes.c_int),
     ]
 
 
@@ -72,7 +74,7 @@ def load(path: str = LIB_PATH):
     lib.hifa4_calibrate_smooth.argtypes = [vp, vp, i64, i64, i64, i64, i64, cf, vp, vp, vp]
     lib.hifa4_calibrate_smooth.restype = ci
     lib.hifa4_quantize_qkv.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp, vp,
-                                       vp, vp, vp, vp, vp, vp, vp]
+                                       vp, vp, vp, vp, vp, vp, ci, vp]
     lib.hifa4_quantize_qkv.restype = ci
     lib.hifa4_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(sz)]
     lib.hifa4_attn_workspace_bytes.restype = ci
@@ -83,7 +85,7 @@ def load(path: str = LIB_PATH):
                                            ctypes.POINTER(AttnArgs), vp]
     lib.hifa4_attn_fwd_noalloc.restype = ci
     lib.hifa4_kv_append.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, ci, vp,
-                                    vp, vp, vp, vp, vp, vp]
+                                    vp, vp, vp, vp, vp, ci, vp]
     lib.hifa4_kv_append.restype = ci
     _lib = lib
     return lib
@@ -123,10 +125,10 @@ def hifa4_calibrate_smooth(q_cal, k_cal, B, Hq, Hkv, N_cal, d, alpha, s_out, inv
 
 
 def hifa4_quantize_qkv(q, k, v, B, Hq, Hkv, N_q, N_kv, d, smooth, s, inv_s, q_codes, q_scales,
-                       k_codes, k_scales, v_codes, v_scales, stream):
+                       k_codes, k_scales, v_codes, v_scales, scale_rule, stream):
     _check(load().hifa4_quantize_qkv(q, k, v, B, Hq, Hkv, N_q, N_kv, d, int(smooth), s, inv_s,
                                      q_codes, q_scales, k_codes, k_scales, v_codes, v_scales,
-                                     stream), "hifa4_quantize_qkv")
+                                     int(scale_rule), stream), "hifa4_quantize_qkv")
 
 
 def hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args: AttnArgs, stream):
@@ -142,10 +144,12 @@ def hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, ar
 
 
 def hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos, rope_sin, rope_rows,
-                    smooth, inv_s, k_codes, k_scales, v_codes, v_scales, v_stage, stream):
+                    smooth, inv_s, k_codes, k_scales, v_codes, v_scales, v_stage, scale_rule,
+                    stream):
     _check(load().hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos,
                                   rope_sin, rope_rows, int(smooth), inv_s, k_codes, k_scales,
-                                  v_codes, v_scales, v_stage, stream), "hifa4_kv_append")
+                                  v_codes, v_scales, v_stage, int(scale_rule), stream),
+           "hifa4_kv_append")
 
 
 # ---------------------------------------------------------------------------
@@ -192,7 +196,7 @@ def calibrate_smooth(q_cal, k_cal, alpha: float, stream=None):
 
 
 def quantize_qkv(q=None, k=None, v=None, *, Hkv: int, smooth: bool = False, s=None, inv_s=None,
-                 out=None, stream=None):
+                 out=None, scale_rule: int = SCALE_OCP, stream=None):
     """Smooth-QK + MXFP4 quantization.  Returns (q4, k4, v4) (None for skipped inputs).
     `out` may pass preallocated (q4, k4, v4) MX4 buffers."""
     ref = next(t for t in (q, k, v) if t is not None)
@@ -211,13 +215,13 @@ def quantize_qkv(q=None, k=None, v=None, *, Hkv: int, smooth: bool = False, s=No
                        _ptr(q4.codes) if q4 else None, _ptr(q4.scales) if q4 else None,
                        _ptr(k4.codes) if k4 else None, _ptr(k4.scales) if k4 else None,
                        _ptr(v4.codes) if v4 else None, _ptr(v4.scales) if v4 else None,
-                       _stream(stream))
+                       scale_rule, _stream(stream))
     return q4, k4, v4
 
 
 def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, workspace=None,
               num_splits: int = 1, kv_tile: int = 64, phat: Optional[MX4] = None,
-              kv_capacity: int = 0) -> AttnArgs:
+              kv_capacity: int = 0, scale_rule: int = SCALE_OCP) -> AttnArgs:
     a = AttnArgs()
     a.q_codes = _ptr(q4.codes) if q4 else None
     a.q_scales = _ptr(q4.scales) if q4 else None
@@ -233,13 +237,15 @@ def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, w
     a.phat_codes = _ptr(phat.codes) if phat else None
     a.phat_scales = _ptr(phat.scales) if phat else None
     a.kv_capacity = kv_capacity
+    a.scale_rule = scale_rule
     return a
 
 
 def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, N_q: int,
              N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool, q_f16=None, s=None,
              num_splits: int = 1, kv_tile: int = 64, out=None, workspace=None,
-             phat: Optional[MX4] = None, kv_capacity: int = 0, stream=None):
+             phat: Optional[MX4] = None, kv_capacity: int = 0, scale_rule: int = SCALE_OCP,
+             stream=None):
     """4-bit attention forward; returns out [B][Hq][N_q][d] binary16.  kv_capacity: token
     rows of the K/V buffers when they are a cache larger than N_kv (0: padded N_kv)."""
     import torch
@@ -250,7 +256,8 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
         nbytes = hifa4_attn_workspace_bytes(B, Hq, N_q, d, num_splits)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=workspace,
-                     num_splits=num_splits, kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity)
+                     num_splits=num_splits, kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity,
+                     scale_rule=scale_rule)
     hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args, _stream(stream))
     return out
 
@@ -258,11 +265,12 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
 def attn_fwd_noalloc(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int,
                      N_q: int, N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool,
                      out, q_f16=None, s=None, num_splits: int = 1, kv_tile: int = 64,
-                     phat: Optional[MX4] = None, kv_capacity: int = 0, stream=None):
+                     phat: Optional[MX4] = None, kv_capacity: int = 0,
+                     scale_rule: int = SCALE_OCP, stream=None):
     """attn_fwd through the entry point that allocates nothing: the caller passes `out`, and
     the split-KV partial states use the library's static device scratch."""
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=None, num_splits=num_splits,
-                     kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity)
+                     kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity, scale_rule=scale_rule)
     hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args,
                            _stream(stream))
     return out
@@ -292,7 +300,8 @@ def empty_kv_cache(B: int, Hkv: int, capacity: int, d: int, device="cuda") -> KV
 
 
 def kv_append(cache: KVCache, k_new=None, v_new=None, *, pos: int, rope_cos=None, rope_sin=None,
-              smooth: bool = False, inv_s=None, stream=None) -> None:
+              smooth: bool = False, inv_s=None, scale_rule: int = SCALE_OCP,
+              stream=None) -> None:
     """Append tokens [pos, pos + T) ([B][Hkv][T][d] binary16; K before RoPE) to the cache."""
     ref = k_new if k_new is not None else v_new
     B, Hkv, T, d = ref.shape
@@ -300,4 +309,4 @@ def kv_append(cache: KVCache, k_new=None, v_new=None, *, pos: int, rope_cos=None
     hifa4_kv_append(_ptr(k_new), _ptr(v_new), B, Hkv, T, d, pos, cache.capacity, _ptr(rope_cos),
                     _ptr(rope_sin), rows, smooth, _ptr(inv_s), _ptr(cache.k4.codes),
                     _ptr(cache.k4.scales), _ptr(cache.v4.codes), _ptr(cache.v4.scales),
-                    _ptr(cache.v_stage), _stream(stream))
+                    _ptr(cache.v_stage), scale_rule, _stream(stream))

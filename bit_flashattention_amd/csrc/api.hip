@@ -122,7 +122,7 @@ hifa4_status scratch_address(void** out) {
 
 extern "C" {
 
-int hifa4_version(void) { return 102; }
+int hifa4_version(void) { return 103; }
 
 const char* hifa4_status_str(hifa4_status s) {
   switch (s) {
@@ -193,7 +193,9 @@ hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void
                                 int64_t d, int smooth, const float* s, const float* inv_s,
                                 uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes,
                                 uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
-                                void* stream) {
+                                int scale_rule, void* stream) {
+  if (scale_rule != HIFA4_SCALE_OCP && scale_rule != HIFA4_SCALE_NOCLIP)
+    return fail(HIFA4_EINVAL, "quantize: scale_rule must be HIFA4_SCALE_OCP or HIFA4_SCALE_NOCLIP");
   if (B < 0 || Hq <= 0 || Hkv <= 0 || N_q < 0 || N_kv < 0 || Hq % Hkv != 0)
     return fail(HIFA4_EINVAL, "quantize: need B, N >= 0, Hq, Hkv > 0, Hq %% Hkv == 0");
   if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "quantize: d must be a positive multiple of 32");
@@ -224,7 +226,7 @@ hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void
   hipError_t e;
   if ((e = hifa4::launch_quant_qkv(q_f16, smooth ? s : nullptr, k_f16, smooth ? inv_s : nullptr,
                                    v_f16, B, Hq, Hkv, N_q, N_kv, d, q_codes, q_scales, k_codes,
-                                   k_scales, v_codes, v_scales, hs)) != hipSuccess)
+                                   k_scales, v_codes, v_scales, scale_rule, hs)) != hipSuccess)
     return hip_fail(e, "quantize");
   return ok();
 }
@@ -253,6 +255,8 @@ static hifa4_status attn_fwd_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_
   if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "attn: d must be a positive multiple of 32");
   if (!supported_d(d)) return fail(HIFA4_EUNSUPPORTED, "attn: d = %lld not built (64, 128, 256)", (long long)d);
   if (B == 0 || N_q == 0) return ok();  // nothing to compute
+  if (a->scale_rule != HIFA4_SCALE_OCP && a->scale_rule != HIFA4_SCALE_NOCLIP)
+    return fail(HIFA4_EINVAL, "attn: scale_rule must be HIFA4_SCALE_OCP or HIFA4_SCALE_NOCLIP");
   const int kv_tile = a->kv_tile == 0 ? hifa4::kKvTile : a->kv_tile;
   if (kv_tile != 64 && kv_tile != 128) return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64 or 128");
   if (a->num_splits < 1) return fail(HIFA4_EINVAL, "attn: num_splits must be >= 1");
@@ -334,6 +338,7 @@ static hifa4_status attn_fwd_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_
   L.reorder = reorder ? 1 : 0;
   L.num_splits = a->num_splits;
   L.kv_tile = kv_tile;
+  L.noclip = a->scale_rule == HIFA4_SCALE_NOCLIP ? 1 : 0;
   hipError_t e;
   if (split_path) {
     e = hifa4::launch_attn_split(L, (hipStream_t)stream);
@@ -363,7 +368,9 @@ hifa4_status hifa4_kv_append(const void* k_new_f16, const void* v_new_f16, int64
                              int64_t kv_capacity, const float* rope_cos, const float* rope_sin,
                              int64_t rope_rows, int smooth, const float* inv_s,
                              uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
-                             uint8_t* v_scales, void* v_stage_f16, void* stream) {
+                             uint8_t* v_scales, void* v_stage_f16, int scale_rule, void* stream) {
+  if (scale_rule != HIFA4_SCALE_OCP && scale_rule != HIFA4_SCALE_NOCLIP)
+    return fail(HIFA4_EINVAL, "kv_append: scale_rule must be HIFA4_SCALE_OCP or HIFA4_SCALE_NOCLIP");
   if (B < 0 || Hkv <= 0 || T < 0 || pos < 0)
     return fail(HIFA4_EINVAL, "kv_append: need B, T, pos >= 0 and Hkv > 0");
   if (d <= 0 || d % 32 != 0) return fail(HIFA4_EINVAL, "kv_append: d must be a positive multiple of 32");
@@ -398,7 +405,8 @@ hifa4_status hifa4_kv_append(const void* k_new_f16, const void* v_new_f16, int64
     if ((st = check_dev_ptr(ptrs[i], names[i]))) return st;
   hipError_t e = hifa4::launch_kv_append(k_new_f16, v_new_f16, B, Hkv, T, d, pos, kv_capacity,
                                          cs, sn, is, k_codes, k_scales, v_codes, v_scales,
-                                         v_new_f16 ? v_stage_f16 : nullptr, (hipStream_t)stream);
+                                         v_new_f16 ? v_stage_f16 : nullptr,
+                                         scale_rule == HIFA4_SCALE_NOCLIP ? 1 : 0, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return ok();
 }

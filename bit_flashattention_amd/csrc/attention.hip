@@ -123,7 +123,7 @@ struct TileP {
 // the E2M1 codes of P_hat and, for reorder = 0, the row sum of P.
 template <int D, int KT, bool REORDER, bool DUMP>
 __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
-                                              float c, float& m, TileP<KT>& tp,
+                                              float c, int noclip, float& m, TileP<KT>& tp,
                                               uint8_t* phat_codes_row, uint8_t* phat_scales_row) {
   constexpr int NB = KT / 32, NU = KT / 64;
   const int hf = (threadIdx.x >> 5) & 1;
@@ -166,18 +166,30 @@ __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool 
   const float m_use = (m_new == kNegInf) ? 0.0f : m_new;  // column with no valid key yet
   const float alpha = exp2_hw(m - m_use);
 
-  // per-block exponents e = floor(t_max) - 2 with the clamp at -127 applied as
-  // t_max >= -125 (t_max <= half an FP16 ulp of m, so e never reaches 127):
-  // sc[bb] = 2^e scales this lane's elements of block bb; psc[u] is the scale
-  // byte of block 2u + hf, the block this lane holds after the code exchange
+  // per-block exponents from t_max = fma(block max S, c, -m) (the largest t of
+  // the block: the map S -> fma(S, c, -m) is monotone), e = fl - 2 with
+  //   OCP rule:     fl = floor(t_max),
+  //   no clipping:  fl = ceil(fp32(t_max - log2 1.5)) = -floor(fp32(log2 1.5 - t_max)),
+  //                 the smallest fl with 2^(t_max - fl + 2) <= 6;
+  // the clamp at e >= -127 is applied as fl >= -125 (t_max <= half an FP16 ulp
+  // of m, so e never reaches 127).  The rule is a kernel argument (the branch is
+  // uniform).  sc[bb] = 2^e scales this lane's elements of block bb; psc[u] is
+  // the scale byte of block 2u + hf, the block this lane holds after the code
+  // exchange
   float sc[NB];
   int fl[NB];
   int* psc = tp.psc;
+  if (noclip) {
+    constexpr float kLog2ThreeHalves = 0.584962500721156181453738943947816508759814407692481060455f;
 #pragma unroll
-  for (int bb = 0; bb < NB; bb++) {
-    fl[bb] = (int)floorf(fmaxf(__builtin_fmaf(bm[bb], c, -m_use), -125.0f));
-    sc[bb] = __builtin_amdgcn_ldexpf(0.25f, fl[bb]);
+    for (int bb = 0; bb < NB; bb++)
+      fl[bb] = -(int)floorf(fminf(kLog2ThreeHalves - __builtin_fmaf(bm[bb], c, -m_use), 125.0f));
+  } else {
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) fl[bb] = (int)floorf(fmaxf(__builtin_fmaf(bm[bb], c, -m_use), -125.0f));
   }
+#pragma unroll
+  for (int bb = 0; bb < NB; bb++) sc[bb] = __builtin_amdgcn_ldexpf(0.25f, fl[bb]);
   const int hmask = -hf;  // all ones in the upper half-wave
 #pragma unroll
   for (int u = 0; u < NU; u++) psc[u] = ((fl[2 * u + 1] & hmask) | (fl[2 * u] & ~hmask)) + 125;
@@ -269,11 +281,12 @@ __device__ __forceinline__ void pv_accumulate(const TileP<KT>& tp, const VOps& v
 // A whole tile: softmax, rescale, normalizer and PV, in that order.
 template <int D, int KT, bool REORDER, bool DUMP, class VOps>
 __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
-                                           float c, const VOps& vops, v16f (&accO)[D / 32],
+                                           float c, int noclip, const VOps& vops, v16f (&accO)[D / 32],
                                            float& m, float& l, uint8_t* phat_codes_row,
                                            uint8_t* phat_scales_row) {
   TileP<KT> tp;
-  softmax_quant<D, KT, REORDER, DUMP>(s, kb0, need_mask, lim, c, m, tp, phat_codes_row, phat_scales_row);
+  softmax_quant<D, KT, REORDER, DUMP>(s, kb0, need_mask, lim, c, noclip, m, tp, phat_codes_row,
+                                      phat_scales_row);
   rescale_o<D>(accO, tp.alpha);
   pv_accumulate<D, KT, REORDER>(tp, vops, accO, l);
 }
@@ -310,7 +323,7 @@ __device__ __forceinline__ void store_out(uint16_t* orow, const v16f (&accO)[D /
 // channels 64 s + 32 hf .. + 32, one whole block, so no lane exchange is
 // needed.  qx = NULL gives a zero row (padding columns).
 template <int D>
-__device__ __forceinline__ void quantize_query_lane(const uint16_t* qx, const float* srow,
+__device__ __forceinline__ void quantize_query_lane(const uint16_t* qx, const float* srow, int noclip,
                                                     uint4 (&qb)[D / 64], uint32_t (&qsc)[(D / 64 + 1) / 2]) {
   constexpr int KS = D / 64, SW = (D / 64 + 1) / 2;
   const int hf = (threadIdx.x >> 5) & 1;
@@ -343,7 +356,7 @@ __device__ __forceinline__ void quantize_query_lane(const uint16_t* qx, const fl
     float amax = 0.0f;
 #pragma unroll
     for (int z = 0; z < 32; z++) amax = fmaxf(amax, fabsf(v[z]));
-    const int e = mx_exponent(amax);
+    const int e = mx_exponent(amax, noclip);
     const float sc = pow2f(e);
     qb[s].x = pack8_fp4(&v[0], sc);
     qb[s].y = pack8_fp4(&v[8], sc);
@@ -371,6 +384,7 @@ struct KParams {
   int G, num_splits, n_tiles, tiles_per_split;
   int heads_per_wg;  // query heads per prefill workgroup (the rest of its 4 waves are row blocks)
   int one_round;     // prefill: every workgroup is resident at once (row groups in complementary order)
+  int noclip;        // block-exponent rule of P_hat and of an in-kernel quantized Q
   float c;
 };
 
@@ -593,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   if (wave_active && p.q_f16) {
     // raw binary16 query: Smooth-QK and quantization here (rows past N_q are zero)
     quantize_query_lane<D>(qrow < p.N_q ? p.q_f16 + (bh * p.N_q + qrow) * D : nullptr,
-                           p.s ? p.s + g * D : nullptr, qb, qsc);
+                           p.s ? p.s + g * D : nullptr, p.noclip, qb, qsc);
   } else if (wave_active) {
     const uint8_t* qr = p.q_codes + (bh * p.Npad_q + qrow) * (D / 2);
 #pragma unroll
@@ -641,7 +655,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
 #pragma unroll
         for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(ka[bb], ksw[bb], qb, qsc);
         LdsVRegs<D, KT> vops(st);
-        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
+        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, p.noclip, vops, accO, m, l, phc, phs);
       } else {
         // d = 256 with 128-key tiles: the operands would not fit in registers
         // next to O (128) and S^T (64), so they are read block by block
@@ -656,7 +670,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
           sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
         }
         const LdsV<D, KT> vops{st};
-        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, vops, accO, m, l, phc, phs);
+        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, p.noclip, vops, accO, m, l, phc, phs);
       }
     }
     __syncthreads();
@@ -825,7 +839,8 @@ __device__ __forceinline__ void split_query(const KParams& p, int64_t b, int64_t
 #pragma unroll
   for (int w = 0; w < SW; w++) qsc[w] = 0u;
   if constexpr (QRAW) {
-    quantize_query_lane<D>(real ? p.q_f16 + row * D : nullptr, p.s ? p.s + g * D : nullptr, qb, qsc);
+    quantize_query_lane<D>(real ? p.q_f16 + row * D : nullptr, p.s ? p.s + g * D : nullptr, p.noclip, qb,
+                           qsc);
   } else {
     const int64_t qr_idx = (b * p.Hq + h) * p.Npad_q + i;
     const uint8_t* qr = p.q_codes + qr_idx * (D / 2);
@@ -902,7 +917,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(KParams p) {
 #pragma unroll
         for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(op.ka[bb], op.ksw[bb], qb, qsc);
         const bool need_mask = (kb0 + KT - 1) > wave_lim;
-        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, op, accO, m, l, phc, phs);
+        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, p.noclip, op, accO, m, l, phc, phs);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -1011,7 +1026,7 @@ __global__ __launch_bounds__(256, (D * KT <= 128 * 64) ? 2 : 1) void attn_decode
 #pragma unroll
           for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(op.ka[bb], op.ksw[bb], qb, qsc);
           const bool need_mask = (kb0 + KT - 1) > wave_lim;
-          softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, op, accO, m, l, phc, phs);
+          softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, p.noclip, op, accO, m, l, phc, phs);
         }
         if (pos % tpc == tpc - 1) {  // chunk done: its state to LDS, then start the next one
           const int k = wave + 4 * (pos / tpc);
@@ -1214,6 +1229,7 @@ KParams make_params(const AttnLaunch& a) {
   kp.tiles_per_split = (kp.n_tiles + a.num_splits - 1) / a.num_splits;
   kp.heads_per_wg = (kp.G % 4 == 0) ? 4 : (kp.G % 2 == 0) ? 2 : 1;
   kp.one_round = 0;
+  kp.noclip = a.noclip;
   kp.c = (float)(1.4426950408889634073599246810019 / __builtin_sqrt((double)a.d));
   return kp;
 }

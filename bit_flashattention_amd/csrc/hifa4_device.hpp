@@ -57,12 +57,16 @@ __device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x;
 // v_exp_f32: 2^x, within 1 ulp, results below 2^-126 flushed to 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// MX block exponent from a block's largest magnitude (non-negative, finite):
-// clamp(floor(log2 a) - 2, -127, 127), with 0 and subnormals giving -127.
-// floor(log2 a) is read from the exponent field (2 = emax of E2M1).
-__device__ __forceinline__ int mx_exponent(float amax) {
-  int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
-  int e = ex - 2;
+// MX block exponent from a block's largest magnitude (non-negative, finite),
+// clamped to [-127, 127], with 0 and subnormals giving -127:
+//   noclip = 0 (the OCP MX rule): floor(log2 a) - 2, read from the exponent
+//     field (2 = emax of E2M1); a block whose a * 2^-e lands in [6, 8) saturates;
+//   noclip = 1: the smallest e with a * 2^-e <= 6, i.e. one more than the OCP
+//     exponent when a's mantissa exceeds 1.5 (6 = 1.5 * 2^2).
+__device__ __forceinline__ int mx_exponent(float amax, int noclip) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int ex = (int)((bits >> 23) & 0xFFu) - 127;
+  const int e = ex - 2 + (noclip & (int)((bits & 0x7FFFFFu) > 0x400000u));
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 

@@ -15,20 +15,21 @@ inline int64_t pad_tokens(int64_t n) { return (n + kTokenPad - 1) / kTokenPad * 
 hipError_t launch_calib_absmax(const void* q, const void* k, int64_t B, int64_t Hq, int64_t Hkv,
                                int64_t N, int64_t d, float* qmax, float* kmax,
                                hipStream_t stream);
+// noclip: block-exponent rule of every 4-bit block written (0: OCP MX, 1: no clipping)
 hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_t H, int64_t Hkv,
-                             int64_t N, int64_t d, uint8_t* codes, uint8_t* scales,
+                             int64_t N, int64_t d, uint8_t* codes, uint8_t* scales, int noclip,
                              hipStream_t stream);
 hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const float* inv_s,
                             const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q,
                             int64_t N_kv, int64_t d, uint8_t* q_codes, uint8_t* q_scales,
                             uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
-                            uint8_t* v_scales, hipStream_t stream);
+                            uint8_t* v_scales, int noclip, hipStream_t stream);
 
 hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t T,
                             int64_t d, int64_t pos, int64_t cap, const float* cos_t,
                             const float* sin_t, const float* inv_s, uint8_t* k_codes,
                             uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales, void* stage,
-                            hipStream_t stream);
+                            int noclip, hipStream_t stream);
 
 // Everything one attention launch needs (device pointers + sizes).
 struct AttnLaunch {
@@ -48,6 +49,7 @@ struct AttnLaunch {
   int64_t B, Hq, Hkv, N_q, N_kv, d;
   int64_t Npad_q, Npad_kv;
   int causal, smooth, reorder, num_splits, kv_tile;
+  int noclip;  // block-exponent rule of P_hat and of an in-kernel quantized Q (0: OCP, 1: no clipping)
 };
 
 hipError_t launch_attn_prefill(const AttnLaunch& a, hipStream_t stream);

@@ -42,14 +42,15 @@ struct AppendArgs {
   int64_t Hkv, T, pos, cap;
   int64_t n_k;            // K items: T * d/16 octets of RoPE channel pairs
   int chunks_k, chunks_v; // workgroups per (b, g) for K and for V
+  int noclip;             // block-exponent rule (0: OCP, 1: no clipping)
 };
 
 // One MX block of 32 values: 16 code bytes (value i in nibble i) and the scale byte.
-__device__ __forceinline__ void mx32(const float (&x)[32], u32x4& codes, uint8_t& scale) {
+__device__ __forceinline__ void mx32(const float (&x)[32], u32x4& codes, uint8_t& scale, int noclip) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(x[i]));
-  const int e = mx_exponent(amax);
+  const int e = mx_exponent(amax, noclip);
   const float sc = pow2f(e);
 #pragma unroll
   for (int w = 0; w < 4; w++) codes[w] = pack8_fp4(&x[8 * w], sc);
@@ -115,7 +116,7 @@ __device__ __forceinline__ void append_k_oct(const AppendArgs& a, int64_t bg, in
   }
   al = quad_max(al);
   ah = quad_max(ah);
-  const int el = mx_exponent(al), eh = mx_exponent(ah);
+  const int el = mx_exponent(al, a.noclip), eh = mx_exponent(ah, a.noclip);
   const int64_t row = bg * a.cap + p;
   const int blk = o / 4, q = o % 4;
   uint8_t* crow = a.k_codes + row * (D / 2);
@@ -163,7 +164,7 @@ __device__ void append_v_tile(const AppendArgs& a, int64_t bg, int64_t tau, uint
     for (int k = 0; k < 32; k++) x[k] = half_to_float(lds[(rb + operand_key(k)) * ROW + ch]);
     u32x4 codes;
     uint8_t sc;
-    mx32(x, codes, sc);
+    mx32(x, codes, sc, a.noclip);
     *reinterpret_cast<u32x4*>(a.v_codes + (tile * D + ch) * 32 + 16 * (beta & 1)) = codes;
     a.v_scales[(tile * D + ch) * 2 + (beta & 1)] = sc;
   }
@@ -212,9 +213,10 @@ hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv
                             int64_t d, int64_t pos, int64_t cap, const float* cos_t,
                             const float* sin_t, const float* inv_s, uint8_t* k_codes,
                             uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales, void* stage,
-                            hipStream_t stream) {
+                            int noclip, hipStream_t stream) {
   if (B == 0 || T == 0 || (!k && !v)) return hipSuccess;
   AppendArgs a;
+  a.noclip = noclip;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.cos_t = cos_t;

@@ -60,7 +60,7 @@ template <int D>
 __device__ __forceinline__ void quant_row_block(const uint16_t* __restrict__ x, const float* __restrict__ mult,
                                                 int64_t H, int64_t G, int64_t N, int64_t Npad, int64_t t,
                                                 uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                int64_t d_rt) {
+                                                int64_t d_rt, int noclip) {
   const int64_t d = D > 0 ? D : d_rt;
   const int64_t per_row = d / 32;
   const int64_t row = t / per_row, blk = t % per_row;
@@ -93,7 +93,7 @@ __device__ __forceinline__ void quant_row_block(const uint16_t* __restrict__ x, 
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-    const int e = mx_exponent(amax);
+    const int e = mx_exponent(amax, noclip);
     const float scale = pow2f(e);
 #pragma unroll
     for (int w = 0; w < 4; w++) out[w] = pack8_fp4(&v[8 * w], scale);
@@ -121,7 +121,8 @@ struct RowQuads {
 template <int D, int NPT>
 __device__ __forceinline__ void quant_row_quads(const uint16_t* __restrict__ x, const float* __restrict__ mult,
                                                 int64_t H, int64_t G, int64_t N, int64_t Npad, int64_t wg,
-                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                int noclip) {
   using RQ = RowQuads<D, NPT>;
   const int64_t wgs_per_head = Npad / RQ::ROWS;
   const int64_t bh = wg / wgs_per_head;  // uniform: one division per workgroup
@@ -170,7 +171,7 @@ __device__ __forceinline__ void quant_row_quads(const uint16_t* __restrict__ x, 
     uint32_t out = 0u;
     uint8_t sc = 0;
     if (live) {
-      const int e = mx_exponent(amax);
+      const int e = mx_exponent(amax, noclip);
       out = pack8_fp4(v, pow2f(e));
       sc = (uint8_t)(e + 127);
     }
@@ -183,10 +184,10 @@ __device__ __forceinline__ void quant_row_quads(const uint16_t* __restrict__ x, 
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ mult, int64_t H, int64_t G,
     int64_t N, int64_t Npad, int64_t d, int64_t total_threads, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, int noclip) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= total_threads) return;
-  quant_row_block<0>(x, mult, H, G, N, Npad, t, codes, scales, d);
+  quant_row_block<0>(x, mult, H, G, N, Npad, t, codes, scales, d, noclip);
 }
 
 // ---------------------------------------------------------------------------
@@ -203,7 +204,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 template <int D>
 __device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, int64_t N, int64_t Npad,
                                              int64_t tile, uint16_t* tile_lds,
-                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                             int noclip) {
   constexpr int ROW = D + 8;  // padded LDS row (binary16 elements): spreads column reads over banks
   const int64_t tiles = Npad / 64;
   const int64_t bh = tile / tiles, t64 = tile % tiles;  // tile = (b*H + h) * tiles + tile index
@@ -236,7 +238,7 @@ __device__ __forceinline__ void quant_v_tile(const uint16_t* __restrict__ v, int
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(x[k]));
-    const int e = mx_exponent(amax);
+    const int e = mx_exponent(amax, noclip);
     const float sc = pow2f(e);
     u32x4 out;
 #pragma unroll
@@ -264,6 +266,7 @@ struct QuantArgs {
   int64_t vN, vNpad, vtiles;
   uint8_t* vcodes;
   uint8_t* vscales;
+  int noclip;  // block-exponent rule (0: OCP, 1: no clipping)
 };
 
 template <int D>
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
   // V tiles first: each is a load -> barrier -> transpose round trip, so they
   // start while the streaming Q / K blocks keep HBM busy
   if (b < a.vtiles) {
-    quant_v_tile<D>(a.v, a.vN, a.vNpad, b, tile_lds, a.vcodes, a.vscales);
+    quant_v_tile<D>(a.v, a.vN, a.vNpad, b, tile_lds, a.vcodes, a.vscales, a.noclip);
     return;
   }
   b -= a.vtiles;
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
   for (int i = 0; i < 2; i++) {
     if (b < a.blocks[i]) {
       quant_row_quads<D, kQuadsPerThread>(a.x[i], a.mult[i], a.H[i], a.G[i], a.N[i], a.Npad[i],
-                                          b, a.codes[i], a.scales[i]);
+                                          b, a.codes[i], a.scales[i], a.noclip);
       return;
     }
     b -= a.blocks[i];
@@ -310,7 +313,7 @@ hipError_t launch_calib_absmax(const void* q, const void* k, int64_t B, int64_t 
 }
 
 hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_t H, int64_t Hkv,
-                             int64_t N, int64_t d, uint8_t* codes, uint8_t* scales,
+                             int64_t N, int64_t d, uint8_t* codes, uint8_t* scales, int noclip,
                              hipStream_t stream) {
   const int64_t Npad = pad_tokens(N);
   const int64_t total = B * H * Npad * (d / 32);
@@ -318,7 +321,7 @@ hipError_t launch_quant_rows(const void* x, const float* mult, int64_t B, int64_
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   quant_rows_kernel<<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
-      (const uint16_t*)x, mult, H, H / Hkv, N, Npad, d, total, codes, scales);
+      (const uint16_t*)x, mult, H, H / Hkv, N, Npad, d, total, codes, scales, noclip);
   return hipGetLastError();
 }
 
@@ -326,14 +329,16 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
                             const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q,
                             int64_t N_kv, int64_t d, uint8_t* q_codes, uint8_t* q_scales,
                             uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
-                            uint8_t* v_scales, hipStream_t stream) {
+                            uint8_t* v_scales, int noclip, hipStream_t stream) {
   if (d != 64 && d != 128 && d != 256) {  // Q / K only (V needs one of these d)
     hipError_t e = hipSuccess;
-    if (q) e = launch_quant_rows(q, s, B, Hq, Hkv, N_q, d, q_codes, q_scales, stream);
-    if (e == hipSuccess && k) e = launch_quant_rows(k, inv_s, B, Hkv, Hkv, N_kv, d, k_codes, k_scales, stream);
+    if (q) e = launch_quant_rows(q, s, B, Hq, Hkv, N_q, d, q_codes, q_scales, noclip, stream);
+    if (e == hipSuccess && k)
+      e = launch_quant_rows(k, inv_s, B, Hkv, Hkv, N_kv, d, k_codes, k_scales, noclip, stream);
     return e;
   }
   QuantArgs a;
+  a.noclip = noclip;
   const void* xs[2] = {q, k};
   const float* ms[2] = {s, inv_s};
   const int64_t Hs[2] = {Hq, Hkv}, Ns[2] = {N_q, N_kv};

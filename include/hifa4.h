@@ -62,6 +62,22 @@ extern "C" {
 
 #define HIFA4_TOKEN_PAD 128
 #define HIFA4_MAX_NKV 32768 /* l <= 1.5 * N_kv must stay below binary16's 65504 */
+/*
+ * Block-exponent rules of the 4-bit blocks (scale_rule arguments).  For a block
+ * whose largest magnitude is a:
+ *   HIFA4_SCALE_OCP    e = floor(log2 a) - 2 (the OCP MX rule; 2 is the exponent
+ *                      of E2M1's largest value 6 = 1.5 * 2^2): a block whose
+ *                      a * 2^-e lands in [6, 8) saturates its largest elements to 6;
+ *   HIFA4_SCALE_NOCLIP the smallest e with a * 2^-e <= 6: nothing saturates.
+ * Both clamped to [-127, 127]; an all-zero block gets -127.  For P_hat the rule is
+ * applied to P = 2^t through t (t = S c - m, per 32-key block):
+ *   OCP: e = floor(t_max) - 2;  NOCLIP: e = ceil(fp32(t_max - fp32(log2 1.5))) - 2.
+ * The HiFA4 abstract names its HIF4 format without defining it; the rules are the
+ * two readings of an MX-style scale choice, and NOCLIP is the ablation of the default.
+ */
+#define HIFA4_SCALE_OCP 0
+#define HIFA4_SCALE_NOCLIP 1
+
 /* Size of the static device scratch of hifa4_attn_fwd_noalloc (16 MiB per device). */
 #define HIFA4_NOALLOC_SCRATCH_BYTES (16u << 20)
 
@@ -110,21 +126,23 @@ hifa4_status hifa4_calibrate_smooth(const void* q_cal_f16, const void* k_cal_f16
  * RoPE, then 4-bit operands for both GEMMs).
  *   Q: x = fp32(q * s[g][j])      (smooth = 1) or fp32(q) (smooth = 0)
  *   K: x = fp32(k * inv_s[g][j])  (a multiply by the stored reciprocal)
- *   Each block of 32: e = clamp(floor(log2 max|x|) - 2, -127, 127) (all-zero
+ *   Each block of 32: e from the block's largest |x| by scale_rule
+ *   (HIFA4_SCALE_OCP: clamp(floor(log2 max|x|) - 2, -127, 127); all-zero
  *   block: -127), scale byte e + 127, codes RNE_E2M1(x * 2^-e) with ties to
  *   the even code and saturation at +-6.
  *   V: no rescale; blocks of 32 consecutive tokens (token layout).
  * Any of q_f16 / k_f16 / v_f16 may be NULL to skip that tensor (its output
  * pointers are then ignored).  s and inv_s are [Hkv][d] fp32, ignored when
  * smooth = 0.  Codes/scales buffers must hold hifa4_mx4_bytes(...) bytes and
- * be 16-byte aligned.  Asynchronous.
+ * be 16-byte aligned.  scale_rule: HIFA4_SCALE_OCP or HIFA4_SCALE_NOCLIP (else
+ * EINVAL).  Asynchronous.
  */
 hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void* v_f16,
                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N_q, int64_t N_kv,
                                 int64_t d, int smooth, const float* s, const float* inv_s,
                                 uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes,
                                 uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
-                                void* stream);
+                                int scale_rule, void* stream);
 
 /* Buffers of one attention call (all device pointers). */
 typedef struct {
@@ -169,6 +187,11 @@ typedef struct {
    * N_kv rounded up to HIFA4_TOKEN_PAD.  The P_hat dump rows use the same
    * count: [..][kv_capacity/2] and [..][kv_capacity/32]. */
   int64_t kv_capacity;
+  /* Block-exponent rule of P_hat and of a Q quantized in the kernel (q_f16):
+   * HIFA4_SCALE_OCP (0, the default of a zeroed struct) or HIFA4_SCALE_NOCLIP.
+   * Pre-quantized Q_hat, K_hat and V_hat carry the rule they were quantized
+   * with; a consistent call uses the same rule for all of them. */
+  int scale_rule;
 } hifa4_attn_args;
 
 /* Workspace bytes hifa4_attn_fwd needs for these sizes (0 when num_splits = 1). */
@@ -182,7 +205,8 @@ hifa4_status hifa4_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t N_q, int6
  *   S      = Q_hat K_hat^T                          (4-bit GEMM, fp32 accumulation)
  *   m_new  = fp16(max(m, fp32(c * max S))),  c = fp32(log2(e) / sqrt(d))
  *   alpha  = 2^(m - m_new);   P = 2^(fma(S, c, -m_new))
- *   P_hat  = per 32 keys: e = clamp(floor(max t) - 2, -127, 127), E2M1_rne(P / 2^e) * 2^e
+ *   P_hat  = per 32 keys: e from max t by args->scale_rule (OCP: clamp(floor(max t)
+ *            - 2, -127, 127)), E2M1_rne(P / 2^e) * 2^e
  *   reorder = 1 (P-Reordering): [O | l] = alpha * [O | l] + P_hat [V_hat | 1]
  *                                (the normalizer is a column of the PV GEMM)
  *   reorder = 0:                 O = alpha * O + P_hat V_hat,  l = alpha * l + sum P
@@ -232,6 +256,8 @@ hifa4_status hifa4_attn_fwd_noalloc(int64_t B, int64_t Hq, int64_t Hkv, int64_t 
  *      and rounded to binary16 (NULL tables: r = k, already rotated).  Then
  *      x = fp32(r * inv_s[g][j]) (smooth = 1) or r, and one MX block per 32
  *      channels into K rows pos .. pos+T-1.
+ *   Every block exponent follows scale_rule (HIFA4_SCALE_OCP or HIFA4_SCALE_NOCLIP,
+ *   else EINVAL), the same rule the rest of the cache was written with.
  *   V: v_new_f16 [B][Hkv][T][d].  Every 32-position block that the new tokens
  *      touch is quantized again from the binary16 values of all its tokens so
  *      far (positions after pos+T-1 count as 0).  The values of the block
@@ -253,7 +279,7 @@ hifa4_status hifa4_kv_append(const void* k_new_f16, const void* v_new_f16, int64
                              int64_t kv_capacity, const float* rope_cos, const float* rope_sin,
                              int64_t rope_rows, int smooth, const float* inv_s,
                              uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
-                             uint8_t* v_scales, void* v_stage_f16, void* stream);
+                             uint8_t* v_scales, void* v_stage_f16, int scale_rule, void* stream);
 
 #ifdef __cplusplus
 }

@@ -102,10 +102,10 @@ def out_error(got_f16: np.ndarray, ref_f16: np.ndarray):
     return float(e.max()), float(e.mean())
 
 
-def oracle_quant(w, s=None, inv=None):
-    q4 = oracle.quantize_rows(w.q, w.Hkv, s)
-    k4 = oracle.quantize_rows(w.k, w.Hkv, inv)
-    v4 = oracle.quantize_v(w.v)
+def oracle_quant(w, s=None, inv=None, rule=0):
+    q4 = oracle.quantize_rows(w.q, w.Hkv, s, rule)
+    k4 = oracle.quantize_rows(w.k, w.Hkv, inv, rule)
+    v4 = oracle.quantize_v(w.v, rule)
     return q4, k4, v4
 
 

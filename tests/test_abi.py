@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(hf):
 
 def test_status_strings_and_version(hf):
     lib = hf.load()
-    assert lib.hifa4_version() == 102
+    assert lib.hifa4_version() == 103
     for s in range(6):
         assert lib.hifa4_status_str(s)
     assert b"unknown" in lib.hifa4_status_str(99)
@@ -89,6 +89,7 @@ def _args(hf, **kw):
     (dict(args=dict(k_codes=0x1008)), "EINVAL"),         # misaligned
     (dict(args=dict(kv_capacity=200)), "EINVAL"),        # not a multiple of 128
     (dict(args=dict(kv_capacity=128)), "EINVAL"),        # below N_kv = 256
+    (dict(args=dict(scale_rule=2)), "EINVAL"),           # no such block-exponent rule
 ])
 def test_attn_validation(hf, case, status):
     shape = dict(B=1, Hq=8, Hkv=2, N_q=64, N_kv=256, d=128, causal=0)
@@ -119,24 +120,27 @@ def test_device_checks_after_validation(hf):
     assert e.value.status in (hf.ENODEV, hf.EINVAL)
     with pytest.raises(hf.HiFA4Error) as e:
         hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 128, 0, None, None, p, p, None, None,
-                              None, None, None)
+                              None, None, 0, None)
     assert e.value.status in (hf.ENODEV, hf.EINVAL)
 
 
 @pytest.mark.parametrize("call", ["quant_smooth_no_s", "quant_bad_d", "quant_missing_out",
-                                  "calib_alpha", "calib_null"])
+                                  "quant_bad_rule", "calib_alpha", "calib_null"])
 def test_quantize_calibrate_validation(hf, call):
     p = 0x10000
     with pytest.raises(hf.HiFA4Error) as e:
         if call == "quant_smooth_no_s":
             hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 128, 1, None, None, p, p, None,
-                                  None, None, None, None)
+                                  None, None, None, 0, None)
         elif call == "quant_bad_d":
             hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 100, 0, None, None, p, p, None,
-                                  None, None, None, None)
+                                  None, None, None, 0, None)
         elif call == "quant_missing_out":
             hf.hifa4_quantize_qkv(None, p, None, 1, 8, 2, 0, 64, 128, 0, None, None, None, None,
-                                  None, None, None, None, None)
+                                  None, None, None, None, 0, None)
+        elif call == "quant_bad_rule":
+            hf.hifa4_quantize_qkv(p, None, None, 1, 8, 2, 64, 0, 128, 0, None, None, p, p, None,
+                                  None, None, None, 2, None)
         elif call == "calib_alpha":
             hf.hifa4_calibrate_smooth(p, p, 1, 8, 2, 16, 128, 1.5, p, p, None)
         else:
@@ -170,11 +174,11 @@ def _append(hf, **kw):
     """hifa4_kv_append with plausible (never dereferenced) pointers, overridden by kw."""
     p = 0x10000
     a = dict(k=p, v=p, B=2, Hkv=2, T=3, d=128, pos=61, cap=256, cos=p, sin=p, rows=64, smooth=1,
-             inv_s=p, kc=p, ks=p, vc=p, vs=p, stage=p)
+             inv_s=p, kc=p, ks=p, vc=p, vs=p, stage=p, rule=0)
     a.update(kw)
     hf.hifa4_kv_append(a["k"], a["v"], a["B"], a["Hkv"], a["T"], a["d"], a["pos"], a["cap"],
                        a["cos"], a["sin"], a["rows"], a["smooth"], a["inv_s"], a["kc"], a["ks"],
-                       a["vc"], a["vs"], a["stage"], None)
+                       a["vc"], a["vs"], a["stage"], a["rule"], None)
 
 
 @pytest.mark.parametrize("case,status", [
@@ -190,6 +194,7 @@ def _append(hf, **kw):
     (dict(kc=None), "EINVAL"),
     (dict(stage=None), "EINVAL"),
     (dict(vc=0x10008), "EINVAL"),               # misaligned
+    (dict(rule=2), "EINVAL"),                   # no such block-exponent rule
 ])
 def test_kv_append_validation(hf, case, status):
     with pytest.raises(hf.HiFA4Error) as e:
