@@ -15,6 +15,7 @@ Each measurement first runs its workload untimed for --device-warmup-ms (default
 that the GPU clocks have ramped up, then W untimed warmup steps, then exactly K timed steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu] [--decode-only]
+                       [--prefill-only]
                        [--append-only] [--device-warmup-ms MS]
 """
 from __future__ import annotations
@@ -531,6 +532,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="primary workload only (profiling runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="the three prefill shapes only, no CPU leg (profiling runs); prints its "
+                         "own line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decode step (profiling runs); prints its own line")
@@ -593,6 +597,22 @@ def main():
                           "higher_is_better": False, "appends": lines,
                           "config": {"workload": "kv_append B=64 Hkv=8 d=128 cache 8192 tokens"}}),
               flush=True)
+        return
+
+    if a.prefill_only:
+        lines = {}
+        for fn in (synth.qwen3_8b, synth.gemma2_9b, synth.llama_batched):
+            wx = fn()
+            msx, attnx, stx = run_prefill(wx, hf, torch, a.steps, a.warmup, reorder=True)
+            lines[wx.name] = {"kernel": f"attn_prefill_kernel<{wx.d},{default_kv_tile(wx.d, wx.N_kv)},"
+                                        f"causal,reorder>", "attn_ms": attnx, "ms_per_step": msx,
+                              "attn_frac_fp4_peak": wx.flops / (attnx * 1e-3) / 1e12 / FP4_PEAK_TFLOPS}
+            log(f"[bench] {wx.name}: attention {attnx:.4f} ms ({100 * lines[wx.name]['attn_frac_fp4_peak']:.2f} "
+                f"% of FP4 peak)")
+            del stx
+            torch.cuda.empty_cache()
+        print(json.dumps({"metric": "prefill attention ms", "steps": a.steps, "warmup": a.warmup,
+                          "workloads": lines}), flush=True)
         return
 
     # ---- primary: Qwen3-8B-shaped causal prefill, P-Reordering on
