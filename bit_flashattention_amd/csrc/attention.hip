@@ -383,7 +383,7 @@ struct KParams {
   int64_t B, Hq, Hkv, N_q, N_kv, Npad_q, Npad_kv;
   int G, num_splits, n_tiles, tiles_per_split;
   int heads_per_wg;  // query heads per prefill workgroup (the rest of its 4 waves are row blocks)
-  int one_round;     // prefill: every workgroup is resident at once (row groups in complementary order)
+  int slot_rows;     // prefill: row groups per residency slot of a one-round grid (0: longest first)
   int noclip;        // block-exponent rule of P_hat and of an in-kernel quantized Q
   float c;
 };
@@ -393,9 +393,11 @@ struct KParams {
 // group x (4 / nh) row blocks of 32 rows.  Grid (B * Hkv * G/nh, row groups);
 // row groups run last-first so the longest causal work starts earliest and
 // the dispatcher's in-order refill balances the rest.  When the whole grid is
-// resident at once (at most two workgroups per CU) there is no refill: then
-// the first half of the grid runs longest first and the second half shortest
-// first, so the two workgroups that share a CU carry complementary row ranges.
+// resident at once there is no refill: the dispatcher hands each CU one
+// workgroup of every consecutive slot of (CU count) workgroups, so the row
+// groups are laid out in a snake over the slots (longest first in even slots,
+// shortest first in odd ones) and the workgroups that share a CU carry
+// complementary row ranges.
 //
 // LDS stage of one tile (KT keys), all in MFMA operand order:
 //   [K_hat codes: KT/32 blocks x D/64 k-steps x 64 lanes x 16 B]
@@ -569,8 +571,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   const int64_t hc = bgc / (p.B * p.Hkv), bg = bgc % (p.B * p.Hkv);
   const int64_t b = bg / p.Hkv, g = bg % p.Hkv;
   const int64_t h = g * p.G + hc * nh + (wave % nh);
-  const int64_t Y = gridDim.y, hy = (Y + 1) / 2, y = blockIdx.y;
-  const int64_t rgrp = (!p.one_round || y < hy) ? Y - 1 - y : y - hy;
+  const int64_t Y = gridDim.y, y = blockIdx.y;
+  int64_t rank = y;  // 0 = the longest row group
+  if (p.slot_rows > 0) {
+    const int64_t sl = y / p.slot_rows, j = y - sl * p.slot_rows;
+    if (sl & 1) rank = sl * p.slot_rows + min64(p.slot_rows, Y - sl * p.slot_rows) - 1 - j;
+  }
+  const int64_t rgrp = Y - 1 - rank;
   const int64_t wg_row0 = rgrp * 32 * nr;
   const int64_t row0 = wg_row0 + 32 * (wave / nh);
   const int64_t bh = b * p.Hq + h;
@@ -1159,17 +1166,43 @@ int device_cu_count() {
   return cus;
 }
 
+// Workgroups of 256 threads of `kernel` resident at once on one CU of the
+// current device (registers and LDS), queried once per device (0 if unknown).
+constexpr int kMaxDevices = 64;
+int resident_per_cu(const void* kernel, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n <= 0) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
+std::atomic<int>* resident_cache() {
+  static std::atomic<int> cache[kMaxDevices];
+  return cache;
+}
+
 template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
 hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   const int nh = kp.heads_per_wg, nr = 4 / nh;
   // x = (head chunk, b, g) with the KV head fastest: consecutive workgroups
   // land on consecutive XCDs, so each XCD's L2 serves a fixed set of KV heads
   dim3 grid((unsigned)(kp.B * kp.Hkv * (kp.G / nh)), (unsigned)((kp.N_q + 32 * nr - 1) / (32 * nr)));
-  // two workgroups fit on a CU (registers and LDS of every instantiation)
+  const auto kernel = attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP>;
   const int cus = device_cu_count();
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel), resident_cache<D, KT, CAUSAL, REORDER, DUMP>());
   KParams k2 = kp;
-  k2.one_round = cus > 0 && (int64_t)grid.x * grid.y <= 2LL * cus;
-  attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP><<<grid, dim3(256), 0, stream>>>(k2);
+  k2.slot_rows = 0;
+  const int64_t wgs = (int64_t)grid.x * grid.y;
+  if (cus > 0 && per_cu > 0 && wgs <= (int64_t)per_cu * cus) {
+    const int64_t slots = (wgs + cus - 1) / cus;  // workgroups each CU receives
+    k2.slot_rows = (int)((grid.y + slots - 1) / slots);
+  }
+  kernel<<<grid, dim3(256), 0, stream>>>(k2);
   return hipGetLastError();
 }
 
@@ -1228,7 +1261,7 @@ KParams make_params(const AttnLaunch& a) {
   kp.n_tiles = (int)((a.N_kv + a.kv_tile - 1) / a.kv_tile);
   kp.tiles_per_split = (kp.n_tiles + a.num_splits - 1) / a.num_splits;
   kp.heads_per_wg = (kp.G % 4 == 0) ? 4 : (kp.G % 2 == 0) ? 2 : 1;
-  kp.one_round = 0;
+  kp.slot_rows = 0;
   kp.noclip = a.noclip;
   kp.c = (float)(1.4426950408889634073599246810019 / __builtin_sqrt((double)a.d));
   return kp;
