@@ -17,9 +17,9 @@
 //    the B operand of O^T = V_hat^T P_hat^T (A = 32 channels x 64 keys of
 //    V_hat, whose tokens are stored in the same in-block order).  The output
 //    accumulator is "lane = query" too: alpha, m and l never leave their lane.
-//  * P-Reordering: one more MFMA with A = all-ones E2M1 codes yields
-//    rowsum(P_hat) -- the normalizer is a row of the same PV product
-//    ([V_hat | 1]) instead of a VALU reduction.
+//  * P-Reordering: one more (16x16x128) MFMA of the same P_hat registers
+//    against E2M1 ones yields rowsum(P_hat) -- the normalizer comes out of the
+//    matrix core, as if from [V_hat | 1], instead of a VALU reduction.
 //  * Prefill: a workgroup is 4 wavefronts that read the same KV head (the
 //    heads of one GQA group, or consecutive row blocks of one head); each
 //    K_hat/V_hat tile is loaded once per workgroup with 1 KB-contiguous
@@ -256,12 +256,21 @@ __device__ __forceinline__ void pv_accumulate(const TileP<KT>& tp, const VOps& v
   // normalizer: l = fp16(fp32(alpha l) + rowsum)
   float rs;
   if constexpr (REORDER) {
-    // P-Reordering: the row sum of P_hat comes out of the matrix core, as one
-    // more row of the PV product (A = all-ones E2M1 codes, scale 2^0).
-    const uint4 ones = {0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u};
-    v16f sl = mfma_fp4<0, 0>(ones, 127, ph[0], psc[0], zero16());
+    // P-Reordering: the row sum of P_hat comes out of the matrix core, from
+    // P_hat against an operand of E2M1 ones (scale 2^0), on the 16x16x128 MFMA
+    // (half the matrix work of a 32x32x64 one).  P_hat's registers, laid out as
+    // the B operand of the 32x32x64 PV product, read as that MFMA's B operand
+    // (lane l: column l % 16, K-slice l / 16) put query c in slices 0 and 2 of
+    // column c and query c + 16 in slices 1 and 3.  Row group g of A (rows
+    // 4g..4g+3, whose results land in lanes 16g..16g+15) holds ones in slices
+    // {0, 2} for even g and {1, 3} for odd g, so lane l receives the row sum of
+    // its own query l % 32.
+    const int ln = threadIdx.x & 63;
+    const uint32_t w = (((ln >> 2) ^ (ln >> 4)) & 1) ? 0u : 0x22222222u;
+    const uint4 ones = {w, w, w, w};
+    v4f sl = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 1; u < NU; u++) sl = mfma_fp4<0, 0>(ones, 127, ph[u], psc[u], sl);
+    for (int u = 0; u < NU; u++) sl = mfma16_fp4_unit_a(ones, ph[u], psc[u], sl);
     rs = sl[0];
   } else {
     rs = tp.rsp;

@@ -44,6 +44,16 @@ __device__ __forceinline__ v16f mfma_fp4_v(const u32x4& a, int sa, const u32x4& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, 0, sa, 0, sb);
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One 16x16x128 E2M1 x E2M1 MFMA with A at scale 2^0: acc += A (B * 2^(sb-127)),
+// the scale byte taken from byte 0 of sb.
+__device__ __forceinline__ v4f mfma16_fp4_unit_a(const uint4& a, const uint4& b, int sb, v4f acc) {
+  v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, 0, 127, 0, sb);
+}
+
 __device__ __forceinline__ v16f zero16() {
   v16f z;
 #pragma unroll
