@@ -140,14 +140,17 @@ __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool 
       }
   }
 
-  // block maxima: this lane's 16 keys, then the partner lane's 16
+  // block maxima: this lane's 16 keys (a balanced tree of three-input maxima,
+  // depth 3 instead of a chain of 8), then the partner lane's 16
   float pm[NB];
 #pragma unroll
   for (int bb = 0; bb < NB; bb++) {
-    float x = fmaxf(s[bb][0], s[bb][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r++) x = fmaxf(x, s[bb][r]);
-    pm[bb] = x;
+    const float a0 = fmaxf(fmaxf(s[bb][0], s[bb][1]), s[bb][2]);
+    const float a1 = fmaxf(fmaxf(s[bb][3], s[bb][4]), s[bb][5]);
+    const float a2 = fmaxf(fmaxf(s[bb][6], s[bb][7]), s[bb][8]);
+    const float a3 = fmaxf(fmaxf(s[bb][9], s[bb][10]), s[bb][11]);
+    const float a4 = fmaxf(fmaxf(s[bb][12], s[bb][13]), s[bb][14]);
+    pm[bb] = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[bb][15]));
   }
   // full block maxima: a swap of a value with itself hands every lane the
   // partial max of both halves of its query's block
