@@ -75,10 +75,12 @@ def prepare_prefill(w, hf, torch):
 
 
 def default_kv_tile(d: int, n_kv: int) -> int:
-    """Keys per tile: 128 for d <= 128 over long key ranges (N_kv >= 4096), else 64.  Measured:
-    the Qwen3-8B shape (N 4096) runs 75.5 us at 128 and 80.6 us at 64; the Llama batch (N 2048)
-    160 us at 64 and 169 us at 128 (its causal diagonal tiles are a larger share of its work)."""
-    return 128 if d <= 128 and n_kv >= 4096 else 64
+    """Keys per tile: 128 over long key ranges (N_kv >= 4096), else 64.  Measured (attention
+    kernel, one box, three runs each): the Qwen3-8B shape (d 128, N 4096) 75.2 us at 128 against
+    78.8 at 64; Gemma2-9B (d 256, N 4096) 72.9 us at 128 against 76.6 at 64; the Llama batch
+    (d 128, N 2048) 160.7 us at 64 against 167.7 at 128 (its causal diagonal tiles are a larger
+    share of its work)."""
+    return 128 if n_kv >= 4096 else 64
 
 
 DEVICE_WARMUP_MS = 100.0
