@@ -115,7 +115,7 @@ def launch_stats(fn, torch, n=100):
 
 
 def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=False,
-                scale_rule=0):
+                scale_rule=0, phat_mode=0):
     """Time `steps` full steps, then `steps` attention launches alone.  A step runs the
     Smooth-QK + quantize pass over Q, K and V, then the attention kernel; with raw_q the
     quantize pass covers K and V only and the attention kernel smooths and quantizes the
@@ -131,7 +131,7 @@ def run_prefill(w, hf, torch, steps, warmup, reorder=True, kv_tile=None, raw_q=F
     def attn():
         hf.attn_fwd(q4a, k4, v4, B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=w.N_q, N_kv=w.N_kv, d=w.d,
                     causal=w.causal, smooth=w.smooth, reorder=reorder, out=st["out"],
-                    kv_tile=kv_tile, scale_rule=scale_rule, **qarg)
+                    kv_tile=kv_tile, scale_rule=scale_rule, phat_mode=phat_mode, **qarg)
 
     def step():
         hf.quantize_qkv(qin, st["k"], st["v"], Hkv=w.Hkv, smooth=w.smooth, s=st["s"],
@@ -682,6 +682,12 @@ def main():
         extra["qwen3_8b_reorder_off"] = {"ms_per_step": ms0, "attn_ms": attn0,
                                          "attn_tflops": w.flops / (attn0 * 1e-3) / 1e12}
         log(f"[bench] reorder off: attention {attn0:.4f} ms")
+        # exp-free P_hat (codes from the log-domain value, no v_exp_f32 per score)
+        msx, attnx, stx = run_prefill(w, hf, torch, a.steps, a.warmup, reorder=True, phat_mode=1)
+        extra["qwen3_8b_expfree_phat"] = {"ms_per_step": msx, "attn_ms": attnx,
+                                          "attn_tflops": w.flops / (attnx * 1e-3) / 1e12}
+        log(f"[bench] exp-free P_hat: attention {attnx:.4f} ms")
+        del stx
         if not a.no_cpu:
             acc_q[0] = rows_to_host(st0["out"], acc_rows, w.d, torch)
             acc_inputs.append(("qwen3_8b_prefill", w, acc_rows, acc_q,

@@ -24,6 +24,8 @@ MAX_NKV = 32768
 OK, EINVAL, EUNSUPPORTED, ENODEV, EHIP, ENOSPACE = range(6)
 # block-exponent rules (hifa4.h): the OCP MX rule, and the smallest exponent that clips nothing
 SCALE_OCP, SCALE_NOCLIP = 0, 1
+# how P_hat's codes are made (hifa4.h): from 2^t by the hardware exponential, or exp-free from t
+PHAT_EXP2, PHAT_EXPFREE = 0, 1
 
 _lib = None
 
@@ -46,6 +48,7 @@ class AttnArgs(ctypes.Structure):
         ("kv_tile", ctypes.c_int), ("num_splits", ctypes.c_int),
         ("phat_codes", ctypes.c_void_p), ("phat_scales", ctypes.c_void_p),
         ("kv_capacity", ctypes.c_int64), ("scale_rule", ctypes.c_int),
+        ("phat_mode", ctypes.c_int),
     ]
 
 
@@ -221,7 +224,8 @@ def quantize_qkv(q=None, k=None, v=None, *, Hkv: int, smooth: bool = False, s=No
 
 def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, workspace=None,
               num_splits: int = 1, kv_tile: int = 64, phat: Optional[MX4] = None,
-              kv_capacity: int = 0, scale_rule: int = SCALE_OCP) -> AttnArgs:
+              kv_capacity: int = 0, scale_rule: int = SCALE_OCP,
+              phat_mode: int = PHAT_EXP2) -> AttnArgs:
     a = AttnArgs()
     a.q_codes = _ptr(q4.codes) if q4 else None
     a.q_scales = _ptr(q4.scales) if q4 else None
@@ -238,6 +242,7 @@ def make_args(q4: Optional[MX4], k4: MX4, v4: MX4, out, *, q_f16=None, s=None, w
     a.phat_scales = _ptr(phat.scales) if phat else None
     a.kv_capacity = kv_capacity
     a.scale_rule = scale_rule
+    a.phat_mode = phat_mode
     return a
 
 
@@ -245,7 +250,7 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
              N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool, q_f16=None, s=None,
              num_splits: int = 1, kv_tile: int = 64, out=None, workspace=None,
              phat: Optional[MX4] = None, kv_capacity: int = 0, scale_rule: int = SCALE_OCP,
-             stream=None):
+             phat_mode: int = PHAT_EXP2, stream=None):
     """4-bit attention forward; returns out [B][Hq][N_q][d] binary16.  kv_capacity: token
     rows of the K/V buffers when they are a cache larger than N_kv (0: padded N_kv)."""
     import torch
@@ -257,7 +262,7 @@ def attn_fwd(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hkv: int, 
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=workspace,
                      num_splits=num_splits, kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity,
-                     scale_rule=scale_rule)
+                     scale_rule=scale_rule, phat_mode=phat_mode)
     hifa4_attn_fwd(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args, _stream(stream))
     return out
 
@@ -266,11 +271,12 @@ def attn_fwd_noalloc(q4: Optional[MX4], k4: MX4, v4: MX4, *, B: int, Hq: int, Hk
                      N_q: int, N_kv: int, d: int, causal: bool, smooth: bool, reorder: bool,
                      out, q_f16=None, s=None, num_splits: int = 1, kv_tile: int = 64,
                      phat: Optional[MX4] = None, kv_capacity: int = 0,
-                     scale_rule: int = SCALE_OCP, stream=None):
+                     scale_rule: int = SCALE_OCP, phat_mode: int = PHAT_EXP2, stream=None):
     """attn_fwd through the entry point that allocates nothing: the caller passes `out`, and
     the split-KV partial states use the library's static device scratch."""
     args = make_args(q4, k4, v4, out, q_f16=q_f16, s=s, workspace=None, num_splits=num_splits,
-                     kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity, scale_rule=scale_rule)
+                     kv_tile=kv_tile, phat=phat, kv_capacity=kv_capacity, scale_rule=scale_rule,
+                     phat_mode=phat_mode)
     hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, args,
                            _stream(stream))
     return out

@@ -122,7 +122,7 @@ hifa4_status scratch_address(void** out) {
 
 extern "C" {
 
-int hifa4_version(void) { return 103; }
+int hifa4_version(void) { return 104; }
 
 const char* hifa4_status_str(hifa4_status s) {
   switch (s) {
@@ -257,6 +257,10 @@ static hifa4_status attn_fwd_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_
   if (B == 0 || N_q == 0) return ok();  // nothing to compute
   if (a->scale_rule != HIFA4_SCALE_OCP && a->scale_rule != HIFA4_SCALE_NOCLIP)
     return fail(HIFA4_EINVAL, "attn: scale_rule must be HIFA4_SCALE_OCP or HIFA4_SCALE_NOCLIP");
+  if (a->phat_mode != HIFA4_PHAT_EXP2 && a->phat_mode != HIFA4_PHAT_EXPFREE)
+    return fail(HIFA4_EINVAL, "attn: phat_mode must be HIFA4_PHAT_EXP2 or HIFA4_PHAT_EXPFREE");
+  if (a->phat_mode == HIFA4_PHAT_EXPFREE && !reorder)
+    return fail(HIFA4_EINVAL, "attn: HIFA4_PHAT_EXPFREE needs reorder = 1 (without it the row sum is of P itself)");
   const int kv_tile = a->kv_tile == 0 ? hifa4::kKvTile : a->kv_tile;
   if (kv_tile != 64 && kv_tile != 128) return fail(HIFA4_EUNSUPPORTED, "attn: kv_tile must be 64 or 128");
   if (a->num_splits < 1) return fail(HIFA4_EINVAL, "attn: num_splits must be >= 1");
@@ -276,6 +280,8 @@ static hifa4_status attn_fwd_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_
   const bool split_path = a->num_splits > 1 || (a->q_f16 != nullptr && G * N_q <= hifa4::kRowsPerWave);
   if (split_path && kv_tile == 128 && d > 128)
     return fail(HIFA4_EUNSUPPORTED, "attn: split-KV with d = 256 needs kv_tile 64");
+  if (split_path && a->phat_mode == HIFA4_PHAT_EXPFREE)
+    return fail(HIFA4_EUNSUPPORTED, "attn: HIFA4_PHAT_EXPFREE is built for the prefill kernel only");
   if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16) || !aligned(a->k_scales, 16) ||
       !aligned(a->v_scales, 16) ||
       (a->q_codes && (!aligned(a->q_codes, 16) || !aligned(a->q_scales, 8))) ||
@@ -339,6 +345,7 @@ static hifa4_status attn_fwd_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N_
   L.num_splits = a->num_splits;
   L.kv_tile = kv_tile;
   L.noclip = a->scale_rule == HIFA4_SCALE_NOCLIP ? 1 : 0;
+  L.phat_mode = a->phat_mode;
   hipError_t e;
   if (split_path) {
     e = hifa4::launch_attn_split(L, (hipStream_t)stream);

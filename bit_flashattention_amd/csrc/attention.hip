@@ -121,7 +121,7 @@ struct TileP {
 
 // The softmax half of a tile: running max (m updated), alpha, P = 2^(S c - m),
 // the E2M1 codes of P_hat and, for reorder = 0, the row sum of P.
-template <int D, int KT, bool REORDER, bool DUMP>
+template <int D, int KT, bool REORDER, bool DUMP, bool EXPFREE = false>
 __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
                                               float c, int noclip, float& m, TileP<KT>& tp,
                                               uint8_t* phat_codes_row, uint8_t* phat_scales_row) {
@@ -197,11 +197,25 @@ __device__ __forceinline__ void softmax_quant(v16f (&s)[KT / 32], int kb0, bool 
 #pragma unroll
   for (int u = 0; u < NU; u++) psc[u] = ((fl[2 * u + 1] & hmask) | (fl[2 * u] & ~hmask)) + 125;
 
-  // P = 2^(S c - m)
+  if constexpr (EXPFREE) {
+    // exp-free P_hat: E2M1 of 2^(t - e) straight from the log-domain value
+    // u = S c - (m + e) (the block exponent folded into the subtrahend), with
+    // the conversion below at scale 1; masked keys (-inf) clamp to 2^-126 -> 0
+    static_assert(REORDER, "the exp-free P_hat has no P for a separate row sum");
 #pragma unroll
-  for (int bb = 0; bb < NB; bb++)
+    for (int bb = 0; bb < NB; bb++) {
+      const float me = m_use + (float)(fl[bb] - 2);
 #pragma unroll
-    for (int r = 0; r < 16; r++) s[bb][r] = exp2_hw(__builtin_fmaf(s[bb][r], c, -m_use));
+      for (int r = 0; r < 16; r++) s[bb][r] = expcast_e2m1(fmaxf(__builtin_fmaf(s[bb][r], c, -me), -126.0f));
+      sc[bb] = 1.0f;
+    }
+  } else {
+    // P = 2^(S c - m)
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) s[bb][r] = exp2_hw(__builtin_fmaf(s[bb][r], c, -m_use));
+  }
 
   // P_hat codes: this lane's 16 keys of each block as two dwords, then one
   // swap per dword pair hands each lane the partner's half of its block
@@ -291,13 +305,13 @@ __device__ __forceinline__ void pv_accumulate(const TileP<KT>& tp, const VOps& v
 }
 
 // A whole tile: softmax, rescale, normalizer and PV, in that order.
-template <int D, int KT, bool REORDER, bool DUMP, class VOps>
+template <int D, int KT, bool REORDER, bool DUMP, class VOps, bool EXPFREE = false>
 __device__ __forceinline__ void softmax_pv(v16f (&s)[KT / 32], int kb0, bool need_mask, int lim,
                                            float c, int noclip, const VOps& vops, v16f (&accO)[D / 32],
                                            float& m, float& l, uint8_t* phat_codes_row,
                                            uint8_t* phat_scales_row) {
   TileP<KT> tp;
-  softmax_quant<D, KT, REORDER, DUMP>(s, kb0, need_mask, lim, c, noclip, m, tp, phat_codes_row,
+  softmax_quant<D, KT, REORDER, DUMP, EXPFREE>(s, kb0, need_mask, lim, c, noclip, m, tp, phat_codes_row,
                                       phat_scales_row);
   rescale_o<D>(accO, tp.alpha);
   pv_accumulate<D, KT, REORDER>(tp, vops, accO, l);
@@ -567,7 +581,7 @@ struct LdsVRegs {
   __device__ __forceinline__ uint32_t sc(int ct) const { return vs[ct]; }
 };
 
-template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool EXPFREE>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
   using S = Stage<D, KT>;
   constexpr int KS = D / 64, CT = D / 32, SW = (D / 64 + 1) / 2, NB = KT / 32;
@@ -674,7 +688,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
 #pragma unroll
         for (int bb = 0; bb < NB; bb++) sacc[bb] = score_block<D>(ka[bb], ksw[bb], qb, qsc);
         LdsVRegs<D, KT> vops(st);
-        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, p.noclip, vops, accO, m, l, phc, phs);
+        softmax_pv<D, KT, REORDER, DUMP, LdsVRegs<D, KT>, EXPFREE>(sacc, kb0, need_mask, lim, p.c, p.noclip, vops,
+                                                                  accO, m, l, phc, phs);
       } else {
         // d = 256 with 128-key tiles: the operands would not fit in registers
         // next to O (128) and S^T (64), so they are read block by block
@@ -689,7 +704,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
           sacc[bb] = score_block<D>(ka, ksw, qb, qsc);
         }
         const LdsV<D, KT> vops{st};
-        softmax_pv<D, KT, REORDER, DUMP>(sacc, kb0, need_mask, lim, p.c, p.noclip, vops, accO, m, l, phc, phs);
+        softmax_pv<D, KT, REORDER, DUMP, LdsV<D, KT>, EXPFREE>(sacc, kb0, need_mask, lim, p.c, p.noclip, vops, accO,
+                                                              m, l, phc, phs);
       }
     }
     __syncthreads();
@@ -1192,21 +1208,21 @@ int resident_per_cu(const void* kernel, std::atomic<int>* cache) {
   return n;
 }
 
-template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool EXPFREE>
 std::atomic<int>* resident_cache() {
   static std::atomic<int> cache[kMaxDevices];
   return cache;
 }
 
-template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP>
+template <int D, int KT, bool CAUSAL, bool REORDER, bool DUMP, bool EXPFREE = false>
 hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   const int nh = kp.heads_per_wg, nr = 4 / nh;
   // x = (head chunk, b, g) with the KV head fastest: consecutive workgroups
   // land on consecutive XCDs, so each XCD's L2 serves a fixed set of KV heads
   dim3 grid((unsigned)(kp.B * kp.Hkv * (kp.G / nh)), (unsigned)((kp.N_q + 32 * nr - 1) / (32 * nr)));
-  const auto kernel = attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP>;
+  const auto kernel = attn_prefill_kernel<D, KT, CAUSAL, REORDER, DUMP, EXPFREE>;
   const int cus = device_cu_count();
-  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel), resident_cache<D, KT, CAUSAL, REORDER, DUMP>());
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kernel), resident_cache<D, KT, CAUSAL, REORDER, DUMP, EXPFREE>());
   KParams k2 = kp;
   k2.slot_rows = 0;
   const int64_t wgs = (int64_t)grid.x * grid.y;
@@ -1282,6 +1298,15 @@ KParams make_params(const AttnLaunch& a) {
 template <int D, int KT>
 hipError_t dispatch_prefill(const AttnLaunch& a, const KParams& kp, hipStream_t st) {
   const bool dump = a.phat_codes != nullptr;
+  if (a.phat_mode == 1) {  // exp-free P_hat (reorder = 1, checked by the caller)
+    const int k2 = (a.causal ? 2 : 0) | (dump ? 1 : 0);
+    switch (k2) {
+      case 0: return launch_prefill_t<D, KT, false, true, false, true>(kp, st);
+      case 1: return launch_prefill_t<D, KT, false, true, true, true>(kp, st);
+      case 2: return launch_prefill_t<D, KT, true, true, false, true>(kp, st);
+      default: return launch_prefill_t<D, KT, true, true, true, true>(kp, st);
+    }
+  }
   const int key = (a.causal ? 4 : 0) | (a.reorder ? 2 : 0) | (dump ? 1 : 0);
   switch (key) {
     case 0: return launch_prefill_t<D, KT, false, false, false>(kp, st);

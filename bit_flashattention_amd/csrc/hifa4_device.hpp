@@ -84,6 +84,22 @@ __device__ __forceinline__ int mx_exponent(float amax, int noclip) {
 // converter below divides by it exactly).
 __device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
 
+// Exp-free stand-in for 2^u, for E2M1 rounding only: exponent from floor(u),
+// mantissa 1 + r(f) from the fraction f = u - floor(u), where the cubic
+// r(f) = f (a + f (b + g f)) equals 2^f - 1 at f = log2 1.25, log2 1.5 and
+// log2 1.75 (and at 0).  Those are the fractions at which 2^u crosses an E2M1
+// rounding boundary (0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5 are 2^k times 1,
+// 1.5, 1.25 or 1.75), and r is increasing, so RNE to E2M1 of the result gives
+// the code of 2^u itself except within a few ulps of a boundary.  u must be
+// finite and at least -126.
+__device__ __forceinline__ float expcast_e2m1(float u) {
+  constexpr float kA = 0.6950093980189241f, kB = 0.22919986977314274f, kG = 0.07502727831798092f;
+  const float f = __builtin_amdgcn_fractf(u);
+  const int k = (int)__builtin_floorf(u);
+  const float m = __builtin_fmaf(f, __builtin_fmaf(f, __builtin_fmaf(f, kG, kB), kA), 1.0f);
+  return __builtin_amdgcn_ldexpf(m, k);
+}
+
 // Two E2M1 codes RNE(a / scale), RNE(b / scale) (ties to even, saturating at
 // +-6, sign kept) written into byte SEL of `old`: a in the low nibble.
 template <int SEL>

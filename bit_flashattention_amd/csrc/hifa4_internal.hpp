@@ -50,6 +50,7 @@ struct AttnLaunch {
   int64_t Npad_q, Npad_kv;
   int causal, smooth, reorder, num_splits, kv_tile;
   int noclip;  // block-exponent rule of P_hat and of an in-kernel quantized Q (0: OCP, 1: no clipping)
+  int phat_mode;  // P_hat from 2^t by v_exp_f32 (0) or exp-free from t (1; prefill, reorder = 1)
 };
 
 hipError_t launch_attn_prefill(const AttnLaunch& a, hipStream_t stream);

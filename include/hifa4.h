@@ -77,6 +77,20 @@ extern "C" {
  */
 #define HIFA4_SCALE_OCP 0
 #define HIFA4_SCALE_NOCLIP 1
+/*
+ * How P_hat's codes are made (phat_mode).  HiFA4's P-Reordering (Abstract) sums the
+ * normalizer from P_hat, so with reorder = 1 only P_hat's codes are needed, not P:
+ *   HIFA4_PHAT_EXP2     P = 2^t by the hardware exponential, then RNE to E2M1 at the
+ *                       block's scale (the reference definition; the default);
+ *   HIFA4_PHAT_EXPFREE  the E2M1 code of 2^(t - e) straight from the log-domain value:
+ *                       exponent floor(t - e), mantissa from a cubic in the fraction
+ *                       that equals 2^f - 1 exactly where 2^(t - e) crosses an E2M1
+ *                       rounding boundary.  Same codes as HIFA4_PHAT_EXP2 except within
+ *                       a few ulps of a boundary; needs reorder = 1 and the prefill
+ *                       kernel (num_splits = 1, not a decode-shaped q_f16 call).
+ */
+#define HIFA4_PHAT_EXP2 0
+#define HIFA4_PHAT_EXPFREE 1
 
 /* Size of the static device scratch of hifa4_attn_fwd_noalloc (16 MiB per device). */
 #define HIFA4_NOALLOC_SCRATCH_BYTES (16u << 20)
@@ -192,6 +206,8 @@ typedef struct {
    * Pre-quantized Q_hat, K_hat and V_hat carry the rule they were quantized
    * with; a consistent call uses the same rule for all of them. */
   int scale_rule;
+  /* HIFA4_PHAT_EXP2 (0, the default of a zeroed struct) or HIFA4_PHAT_EXPFREE. */
+  int phat_mode;
 } hifa4_attn_args;
 
 /* Workspace bytes hifa4_attn_fwd needs for these sizes (0 when num_splits = 1). */

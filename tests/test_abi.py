@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(hf):
 
 def test_status_strings_and_version(hf):
     lib = hf.load()
-    assert lib.hifa4_version() == 103
+    assert lib.hifa4_version() == 104
     for s in range(6):
         assert lib.hifa4_status_str(s)
     assert b"unknown" in lib.hifa4_status_str(99)
@@ -90,15 +90,18 @@ def _args(hf, **kw):
     (dict(args=dict(kv_capacity=200)), "EINVAL"),        # not a multiple of 128
     (dict(args=dict(kv_capacity=128)), "EINVAL"),        # below N_kv = 256
     (dict(args=dict(scale_rule=2)), "EINVAL"),           # no such block-exponent rule
+    (dict(args=dict(phat_mode=2)), "EINVAL"),            # no such P_hat mode
+    (dict(args=dict(phat_mode=1), reorder=0), "EINVAL"),  # exp-free P_hat without P-Reordering
+    (dict(args=dict(phat_mode=1, num_splits=2), N_q=4), "EUNSUPPORTED"),  # exp-free, split-KV
 ])
 def test_attn_validation(hf, case, status):
-    shape = dict(B=1, Hq=8, Hkv=2, N_q=64, N_kv=256, d=128, causal=0)
+    shape = dict(B=1, Hq=8, Hkv=2, N_q=64, N_kv=256, d=128, causal=0, reorder=1)
     argkw = case.pop("args", {})
     shape.update(case)
     a = _args(hf, **argkw)
     with pytest.raises(hf.HiFA4Error) as e:
         hf.hifa4_attn_fwd(shape["B"], shape["Hq"], shape["Hkv"], shape["N_q"], shape["N_kv"],
-                          shape["d"], shape["causal"], 0, 1, a, None)
+                          shape["d"], shape["causal"], 0, shape["reorder"], a, None)
     assert e.value.status == getattr(hf, status)
     assert hf.load().hifa4_last_error()
 
