@@ -149,10 +149,12 @@ def hifa4_attn_fwd_noalloc(B, Hq, Hkv, N_q, N_kv, d, causal, smooth, reorder, ar
 def hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos, rope_sin, rope_rows,
                     smooth, inv_s, k_codes, k_scales, v_codes, v_scales, v_stage, scale_rule,
                     stream):
-    _check(load().hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos,
-                                  rope_sin, rope_rows, int(smooth), inv_s, k_codes, k_scales,
-                                  v_codes, v_scales, v_stage, int(scale_rule), stream),
-           "hifa4_kv_append")
+    st = (_lib or load()).hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos,
+                                          rope_sin, rope_rows, int(smooth), inv_s, k_codes,
+                                          k_scales, v_codes, v_scales, v_stage, int(scale_rule),
+                                          stream)
+    if st != OK:
+        _check(st, "hifa4_kv_append")
 
 
 # ---------------------------------------------------------------------------
@@ -164,9 +166,15 @@ def _ptr(t) -> Optional[int]:
 
 
 def _stream(stream=None) -> int:
+    """Raw HIP stream handle: the given torch stream's, else torch's current stream on the
+    current device (read without building a torch.cuda.Stream object, which costs more host
+    time than a short kernel launch)."""
+    if stream is not None:
+        return stream.cuda_stream
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if not torch.cuda.is_initialized():
+        torch.cuda.init()
+    return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
 
 
 @dataclass
@@ -309,10 +317,17 @@ def kv_append(cache: KVCache, k_new=None, v_new=None, *, pos: int, rope_cos=None
               smooth: bool = False, inv_s=None, scale_rule: int = SCALE_OCP,
               stream=None) -> None:
     """Append tokens [pos, pos + T) ([B][Hkv][T][d] binary16; K before RoPE) to the cache."""
+    # written out inline: at one token per sequence this call is host-bound, and every
+    # Python-level step here costs a measurable part of the kernel's own time
     ref = k_new if k_new is not None else v_new
     B, Hkv, T, d = ref.shape
-    rows = 0 if rope_cos is None else rope_cos.shape[0]
-    hifa4_kv_append(_ptr(k_new), _ptr(v_new), B, Hkv, T, d, pos, cache.capacity, _ptr(rope_cos),
-                    _ptr(rope_sin), rows, smooth, _ptr(inv_s), _ptr(cache.k4.codes),
-                    _ptr(cache.k4.scales), _ptr(cache.v4.codes), _ptr(cache.v4.scales),
-                    _ptr(cache.v_stage), scale_rule, _stream(stream))
+    if rope_cos is None:
+        rows, cos_p, sin_p = 0, None, _ptr(rope_sin)
+    else:
+        rows, cos_p, sin_p = rope_cos.shape[0], rope_cos.data_ptr(), _ptr(rope_sin)
+    k4, v4 = cache.k4, cache.v4
+    hifa4_kv_append(None if k_new is None else k_new.data_ptr(),
+                    None if v_new is None else v_new.data_ptr(), B, Hkv, T, d, pos, cache.capacity,
+                    cos_p, sin_p, rows, smooth, None if inv_s is None else inv_s.data_ptr(),
+                    k4.codes.data_ptr(), k4.scales.data_ptr(), v4.codes.data_ptr(),
+                    v4.scales.data_ptr(), cache.v_stage.data_ptr(), scale_rule, _stream(stream))

@@ -3,6 +3,7 @@
 // HiFA4 attention operator (arXiv 2607.04302, Abstract); this file adds no
 // arithmetic of its own except the host-side finalization of the Smooth-QK
 // scales from the device-reduced maxima.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -32,10 +33,15 @@ hifa4_status ok() {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Once a device has been seen the answer cannot change within the process.
+std::atomic<bool> g_have_device{false};
+
 hifa4_status check_device() {
+  if (g_have_device.load(std::memory_order_relaxed)) return HIFA4_OK;
   int n = 0;
   hipError_t e = hipGetDeviceCount(&n);
   if (e != hipSuccess || n <= 0) return fail(HIFA4_ENODEV, "no HIP device visible");
+  g_have_device.store(true, std::memory_order_relaxed);
   return HIFA4_OK;
 }
 

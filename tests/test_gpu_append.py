@@ -207,3 +207,16 @@ def test_append_full_size(hf):
         assert np.array_equal(to_host(cache.v4.scales[b, g, : w.N // 64]), v4s[1][0, 0])
     del cache
     torch.cuda.empty_cache()
+
+
+def test_binding_stream_is_torch_current_stream(hf):
+    """The binding reads torch's current stream through its raw handle (cheaper than a
+    torch.cuda.Stream object per call); it must be the same stream, also inside a stream
+    context, and an explicit stream argument wins."""
+    import torch
+    assert hf._stream() == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert hf._stream() == side.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert hf._stream(side) == side.cuda_stream
+    assert hf._stream() == torch.cuda.current_stream().cuda_stream
