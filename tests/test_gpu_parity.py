@@ -262,6 +262,9 @@ DECODE_CASES = [
     # one sequence, many chunks: the merge kernel over more chunks than channels
     dict(B=1, Hq=4, Hkv=1, N_kv=8192, d=64, num_splits=128, kv_tile=64),
     dict(B=1, Hq=8, Hkv=2, N_kv=16384, d=128, num_splits=64, kv_tile=128),
+    # more chunks than the merge stages at once (128): a second, ragged batch, and
+    # chunks past the last tile (256 tiles dealt 2 per chunk to 200 chunks)
+    dict(B=1, Hq=4, Hkv=1, N_kv=16384, d=128, num_splits=200, kv_tile=64),
 ]
 
 
