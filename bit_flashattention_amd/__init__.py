@@ -172,9 +172,12 @@ def _stream(stream=None) -> int:
     if stream is not None:
         return stream.cuda_stream
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is None:  # a torch without the raw accessor: the public (slower) path
+        return torch.cuda.current_stream().cuda_stream
     if not torch.cuda.is_initialized():
         torch.cuda.init()
-    return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+    return raw(torch._C._cuda_getDevice())
 
 
 @dataclass
