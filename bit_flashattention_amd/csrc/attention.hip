@@ -347,37 +347,55 @@ __device__ __forceinline__ void store_out(uint16_t* orow, const v16f (&accO)[D /
 // exactly as the quantize pass does it (x = fp32(q * s[j]), one block per 32
 // channels): the lane of half hf builds the B operand of k-step s from
 // channels 64 s + 32 hf .. + 32, one whole block, so no lane exchange is
-// needed.  qx = NULL gives a zero row (padding columns).
+// needed.  Every load (the row's binary16 values and its Smooth-QK scales for
+// all k-steps) is issued before any is used: one wait on memory instead of two
+// per k-step.  qx = NULL gives a zero row (padding columns).
 template <int D>
 __device__ __forceinline__ void quantize_query_lane(const uint16_t* qx, const float* srow, int noclip,
                                                     uint4 (&qb)[D / 64], uint32_t (&qsc)[(D / 64 + 1) / 2]) {
   constexpr int KS = D / 64, SW = (D / 64 + 1) / 2;
   const int hf = (threadIdx.x >> 5) & 1;
+  uint4 raw[KS][4];
+  float4 sv[KS][8];
+  if (qx) {
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) raw[s][u] = *reinterpret_cast<const uint4*>(qx + (2 * s + hf) * 32 + 8 * u);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) raw[s][u] = make_uint4(0, 0, 0, 0);
+  }
+  if (srow) {
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+      for (int u = 0; u < 8; u++) sv[s][u] = *reinterpret_cast<const float4*>(srow + (2 * s + hf) * 32 + 4 * u);
+  }
 #pragma unroll
   for (int w = 0; w < SW; w++) qsc[w] = 0u;
 #pragma unroll
   for (int s = 0; s < KS; s++) {
-    const int cb = 2 * s + hf;
     float v[32];
-    if (qx) {
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(qx + cb * 32 + 8 * u);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int u = 0; u < 4; u++) {
+      const uint32_t w[4] = {raw[s][u].x, raw[s][u].y, raw[s][u].z, raw[s][u].w};
 #pragma unroll
-        for (int z = 0; z < 4; z++) {
-          v[8 * u + 2 * z] = half_to_float((uint16_t)(w[z] & 0xFFFFu));
-          v[8 * u + 2 * z + 1] = half_to_float((uint16_t)(w[z] >> 16));
-        }
+      for (int z = 0; z < 4; z++) {
+        v[8 * u + 2 * z] = half_to_float((uint16_t)(w[z] & 0xFFFFu));
+        v[8 * u + 2 * z + 1] = half_to_float((uint16_t)(w[z] >> 16));
       }
-      if (srow) {
-        const float* sp = srow + cb * 32;
+    }
+    if (srow) {
 #pragma unroll
-        for (int z = 0; z < 32; z++) v[z] = v[z] * sp[z];
+      for (int u = 0; u < 8; u++) {
+        v[4 * u] = v[4 * u] * sv[s][u].x;
+        v[4 * u + 1] = v[4 * u + 1] * sv[s][u].y;
+        v[4 * u + 2] = v[4 * u + 2] * sv[s][u].z;
+        v[4 * u + 3] = v[4 * u + 3] * sv[s][u].w;
       }
-    } else {
-#pragma unroll
-      for (int z = 0; z < 32; z++) v[z] = 0.0f;
     }
     float amax = 0.0f;
 #pragma unroll
