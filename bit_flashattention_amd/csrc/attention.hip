@@ -737,7 +737,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV: one wavefront per (b, g, chunk).  Its 32 query columns are the
+// Split-KV: one wavefront per (b, g, chunk), each in a workgroup of its own
+// (the wavefronts share nothing).  Its 32 query columns are the
 // G * N_q (head-in-group, row) pairs of KV head g (G * N_q <= 32; the rest are
 // zero padding).  Q is smoothed and quantized in-kernel from binary16 (or
 // read pre-quantized).  Each chunk writes its (m, l, O) partial state.
