@@ -239,6 +239,69 @@ def test_prefill_deterministic(hf):
     assert np.array_equal(to_host(a).view(np.uint16), to_host(b).view(np.uint16))
 
 
+def _degenerate_scores(w, kind, seed):
+    """Make a workload's score distribution degenerate (the binary16 tensors only; the
+    calibration batch is left as it is).
+    flat:  Q = 0, so every score is 0, every P is 1 and every P_hat block has the same
+           exponent (P_hat = 1 exactly, the row sum is the number of valid keys).
+    spiky: the K rows of about 5 % of the keys are scaled by 100, so those keys' scores
+           exceed the rest of their row by hundreds of log2 units: most P underflow below
+           2^-126 (taken as 0), P_hat block exponents reach their clamp at -127, the running
+           max jumps by large steps and alpha underflows to 0."""
+    if kind == "flat":
+        w.q = np.zeros_like(w.q)
+    else:
+        rng = np.random.default_rng(seed)
+        k = w.k.astype(np.float32)
+        k[:, :, rng.random(k.shape[2]) < 0.05, :] *= 100.0
+        assert np.abs(k).max() < 60000.0
+        w.k = k.astype(np.float16)
+    return w
+
+
+@pytest.mark.parametrize("kind", ["flat", "spiky"])
+@pytest.mark.parametrize("reorder,kv_tile,d", [(1, 64, 128), (1, 128, 128), (0, 128, 128), (1, 128, 256)])
+def test_prefill_degenerate_scores(hf, kind, reorder, kv_tile, d):
+    """Prefill on degenerate score distributions (causal, ragged): every P_hat code and
+    scale against the oracle, output within the bars."""
+    print(f"[degenerate prefill] {kind} reorder={reorder} kv_tile={kv_tile} d={d}", flush=True)
+    w = _degenerate_scores(synth.qwen3_8b(B=1, Hq=4, Hkv=2, N=300, N_kv=333, d=d, n_cal=64), kind, 3)
+    out, phat, ref = _prefill_case(hf, w, reorder, kv_tile=kv_tile)
+    got = to_host(out).reshape(-1, w.d)
+    n = len(got)
+    check_attn(f"degenerate {kind} prefill reorder={reorder} kv_tile={kv_tile} d={d}", got, ref,
+               valid_keys(np.arange(n), w.N_q, w.N_kv, w.causal),
+               phat=(to_host(phat.codes).reshape(n, -1), to_host(phat.scales).reshape(n, -1)))
+
+
+@pytest.mark.parametrize("kind", ["flat", "spiky"])
+@pytest.mark.parametrize("B,Hkv,C", [(1, 2, 24), (16, 8, 5)])
+def test_decode_degenerate_scores(hf, kind, B, Hkv, C):
+    """Split-KV decode (split and merge kernels at B = 1, the fused kernel at 128 KV heads)
+    on degenerate score distributions, binary16 query quantized in the kernel."""
+    import torch
+    print(f"[degenerate decode] {kind} B={B} Hkv={Hkv} splits={C}", flush=True)
+    w = _degenerate_scores(synth.decode(B=B, Hq=4 * Hkv, Hkv=Hkv, N_kv=1500, d=128, n_cal=64), kind, 4)
+    s_ref, inv_ref = oracle.calibrate(w.q_cal, w.k_cal, w.alpha)
+    rk = oracle.quantize_rows(w.k, w.Hkv, inv_ref)
+    rv = oracle.quantize_v(w.v)
+    rq = oracle.quantize_rows(w.q, w.Hkv, s_ref)
+    npk = oracle.padded(w.N_kv)
+    phat = hf.MX4(torch.zeros((w.B, w.Hq, 1, npk // 2), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((w.B, w.Hq, 1, npk // 32), dtype=torch.uint8, device="cuda"))
+    out = hf.attn_fwd(None, mx4_to_dev(rk), v_to_dev(rv), B=w.B, Hq=w.Hq, Hkv=w.Hkv, N_q=1,
+                      N_kv=w.N_kv, d=w.d, causal=False, smooth=True, reorder=True,
+                      q_f16=to_dev(w.q), s=to_dev(s_ref), num_splits=C, phat=phat, kv_tile=64)
+    _sync()
+    ref = oracle.attn(w.B, w.Hq, w.Hkv, 1, w.N_kv, w.d, causal=False, reorder=1, num_splits=C,
+                      kv_tile=64, q4=rq, k4=rk, v4=rv, want_phat=True)
+    got = to_host(out).reshape(-1, w.d)
+    n = len(got)
+    check_attn(f"degenerate {kind} decode B={B} Hkv={Hkv} splits={C}", got, ref,
+               valid_keys(np.arange(n), 1, w.N_kv, False),
+               phat=(to_host(phat.codes).reshape(n, -1), to_host(phat.scales).reshape(n, -1)))
+
+
 def test_v_ones_gives_one(hf):
     """P-Reordering on the GPU: V = 1 yields output 1 up to the FP16 normalizer."""
     import torch
