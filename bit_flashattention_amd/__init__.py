@@ -55,7 +55,7 @@ class AttnArgs(ctypes.Structure):
 EXPORTS = (
     "hifa4_version", "hifa4_status_str", "hifa4_last_error", "hifa4_mx4_bytes",
     "hifa4_calibrate_smooth", "hifa4_quantize_qkv", "hifa4_attn_workspace_bytes",
-    "hifa4_attn_fwd", "hifa4_attn_fwd_noalloc", "hifa4_kv_append",
+    "hifa4_attn_fwd", "hifa4_attn_fwd_noalloc", "hifa4_kv_append", "hifa4_v_layout",
 )
 
 
@@ -90,6 +90,8 @@ def load(path: str = LIB_PATH):
     lib.hifa4_kv_append.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, ci, vp,
                                     vp, vp, vp, vp, vp, ci, vp]
     lib.hifa4_kv_append.restype = ci
+    lib.hifa4_v_layout.argtypes = [ci, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    lib.hifa4_v_layout.restype = ci
     _lib = lib
     return lib
 
@@ -157,6 +159,11 @@ def hifa4_kv_append(k_new, v_new, B, Hkv, T, d, pos, kv_capacity, rope_cos, rope
         _check(st, "hifa4_kv_append")
 
 
+def hifa4_v_layout(to_tiled, codes_in, scales_in, codes_out, scales_out, B, H, N, d, stream):
+    _check(load().hifa4_v_layout(int(to_tiled), codes_in, scales_in, codes_out, scales_out, B, H, N,
+                                 d, stream), "hifa4_v_layout")
+
+
 # ---------------------------------------------------------------------------
 # torch-tensor conveniences (allocation with torch, then the same C calls)
 # ---------------------------------------------------------------------------
@@ -195,6 +202,29 @@ def empty_mx4(v_layout: bool, B: int, H: int, N: int, d: int, device="cuda") -> 
                    torch.empty((B, H, npad // 64, d, 2), dtype=torch.uint8, device=device))
     return MX4(torch.empty((B, H, npad, d // 2), dtype=torch.uint8, device=device),
                torch.empty((B, H, npad, d // 32), dtype=torch.uint8, device=device))
+
+
+def v_layout(v4: MX4, to_tiled: bool, stream=None) -> MX4:
+    """V_hat converted between the canonical token-blocked layout (codes [B][H][d][Npad/2],
+    scales [B][H][d][Npad/32]) and the tiled layout the attention kernels read (codes
+    [B][H][Npad/64][d][32], scales [B][H][Npad/64][d][2]): hifa4_v_layout.  to_tiled=True
+    takes a canonical tensor, False a tiled one; returns a new MX4 in the other layout."""
+    import torch
+    c = v4.codes
+    if to_tiled:
+        B, H, d, half = c.shape
+        npad = 2 * half
+    else:
+        B, H, nt, d, _ = c.shape
+        npad = 64 * nt
+    if to_tiled:
+        out = empty_mx4(True, B, H, npad, d, device=c.device)
+    else:
+        out = MX4(torch.empty((B, H, d, npad // 2), dtype=torch.uint8, device=c.device),
+                  torch.empty((B, H, d, npad // 32), dtype=torch.uint8, device=c.device))
+    hifa4_v_layout(to_tiled, _ptr(v4.codes), _ptr(v4.scales), _ptr(out.codes), _ptr(out.scales), B, H,
+                   npad, d, _stream(stream))
+    return out
 
 
 def calibrate_smooth(q_cal, k_cal, alpha: float, stream=None):

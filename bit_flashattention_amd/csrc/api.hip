@@ -128,7 +128,7 @@ hifa4_status scratch_address(void** out) {
 
 extern "C" {
 
-int hifa4_version(void) { return 104; }
+int hifa4_version(void) { return 105; }
 
 const char* hifa4_status_str(hifa4_status s) {
   switch (s) {
@@ -152,6 +152,35 @@ hifa4_status hifa4_mx4_bytes(int v_layout, int64_t B, int64_t H, int64_t N, int6
   const int64_t np = hifa4::pad_tokens(N);
   *code_bytes = (size_t)(B * H * np * (d / 2));
   *scale_bytes = (size_t)(B * H * np * (d / 32));
+  return ok();
+}
+
+hifa4_status hifa4_v_layout(int to_tiled, const uint8_t* codes_in, const uint8_t* scales_in,
+                            uint8_t* codes_out, uint8_t* scales_out, int64_t B, int64_t H,
+                            int64_t N, int64_t d, void* stream) {
+  if (!codes_in || !scales_in || !codes_out || !scales_out) return fail(HIFA4_EINVAL, "v_layout: NULL buffer");
+  if (B < 0 || H < 0 || N < 0) return fail(HIFA4_EINVAL, "v_layout: negative size");
+  if (!supported_d(d)) return fail(HIFA4_EINVAL, "v_layout: d must be 64, 128 or 256");
+  if (!aligned(codes_in, 16) || !aligned(scales_in, 16) || !aligned(codes_out, 16) || !aligned(scales_out, 16))
+    return fail(HIFA4_EINVAL, "v_layout: buffers must be 16-byte aligned");
+  const int64_t np = hifa4::pad_tokens(N);
+  const uintptr_t cb = (uintptr_t)(B * H * np * (d / 2)), sb = (uintptr_t)(B * H * np * (d / 32));
+  const uintptr_t ci = (uintptr_t)codes_in, co = (uintptr_t)codes_out, si = (uintptr_t)scales_in,
+                  so = (uintptr_t)scales_out;
+  // [a, a + na) and [b, b + nb) share a byte
+  auto overlap = [](uintptr_t a, uintptr_t na, uintptr_t b, uintptr_t nb) { return a < b + nb && b < a + na; };
+  if (cb > 0 && (overlap(ci, cb, co, cb) || overlap(ci, cb, so, sb) || overlap(si, sb, co, cb) ||
+                 overlap(si, sb, so, sb)))
+    return fail(HIFA4_EINVAL, "v_layout: output overlaps input");
+  if (B * H * N == 0) return ok();
+  hifa4_status st = check_device();
+  if (st) return st;
+  if ((st = check_dev_ptr(codes_in, "codes_in")) || (st = check_dev_ptr(scales_in, "scales_in")) ||
+      (st = check_dev_ptr(codes_out, "codes_out")) || (st = check_dev_ptr(scales_out, "scales_out")))
+    return st;
+  hipError_t e = hifa4::launch_v_layout(to_tiled ? 1 : 0, codes_in, scales_in, codes_out, scales_out, B, H, N,
+                                        d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "v_layout launch");
   return ok();
 }
 

@@ -25,6 +25,10 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
                             uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes,
                             uint8_t* v_scales, int noclip, hipStream_t stream);
 
+// V_hat canonical <-> tiled layout (to_tiled = 1: canonical -> tiled)
+hipError_t launch_v_layout(int to_tiled, const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out,
+                           uint8_t* scales_out, int64_t B, int64_t H, int64_t N, int64_t d, hipStream_t stream);
+
 hipError_t launch_kv_append(const void* k, const void* v, int64_t B, int64_t Hkv, int64_t T,
                             int64_t d, int64_t pos, int64_t cap, const float* cos_t,
                             const float* sin_t, const float* inv_s, uint8_t* k_codes,

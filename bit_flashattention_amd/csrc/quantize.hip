@@ -375,4 +375,67 @@ hipError_t launch_quant_qkv(const void* q, const float* s, const void* k, const 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// V_hat layout conversion between the canonical token-blocked layout (codes
+// [BH][d][Npad/2], scales [BH][d][Npad/32]) and the tiled layout the kernels
+// read (codes [BH][Npad/64][d][32], scales [BH][Npad/64][d][2], each 32-token
+// block's nibbles in operand order: nibble k holds token (k3 k2 k4 k1 k0)).
+// A pure re-arrangement: 16-bit groups of four nibbles move as a whole, since
+// the order keeps bits 1..0 of the token in place.  Operand group G (nibbles
+// 4G..4G+3) holds canonical group (G1 G0 G2) of the block.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ uint4 canonical_to_operand(uint4 c) {
+  return make_uint4((c.x & 0xFFFFu) | (c.y << 16), (c.z & 0xFFFFu) | (c.w << 16), (c.x >> 16) | (c.y & 0xFFFF0000u),
+                    (c.z >> 16) | (c.w & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ uint4 operand_to_canonical(uint4 o) {
+  return make_uint4((o.x & 0xFFFFu) | (o.z << 16), (o.x >> 16) | (o.z & 0xFFFF0000u), (o.y & 0xFFFFu) | (o.w << 16),
+                    (o.y >> 16) | (o.w & 0xFFFF0000u));
+}
+
+// One thread per (head, 64-token tile, channel): its two 32-token blocks (32
+// code bytes) and their two scale bytes.  Channel fastest, so the tiled side
+// is contiguous across a wavefront.
+__global__ __launch_bounds__(256) void v_layout_kernel(int to_tiled, const uint8_t* __restrict__ ci,
+                                                      const uint8_t* __restrict__ si, uint8_t* __restrict__ co,
+                                                      uint8_t* __restrict__ so, int64_t BH, int64_t ntile, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= BH * ntile * d) return;
+  const int c = (int)(idx % d);
+  const int64_t r = idx / d, t = r % ntile, bh = r / ntile;
+  const int64_t tiled_c = ((bh * ntile + t) * d + c) * 32, tiled_s = ((bh * ntile + t) * d + c) * 2;
+  const int64_t canon_c = (bh * d + c) * (ntile * 32) + t * 32, canon_s = (bh * d + c) * (ntile * 2) + t * 2;
+  if (to_tiled) {
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++) {
+      const uint4 x = *reinterpret_cast<const uint4*>(ci + canon_c + 16 * blk);
+      *reinterpret_cast<uint4*>(co + tiled_c + 16 * blk) = canonical_to_operand(x);
+    }
+    so[tiled_s] = si[canon_s];
+    so[tiled_s + 1] = si[canon_s + 1];
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++) {
+      const uint4 x = *reinterpret_cast<const uint4*>(ci + tiled_c + 16 * blk);
+      *reinterpret_cast<uint4*>(co + canon_c + 16 * blk) = operand_to_canonical(x);
+    }
+    so[canon_s] = si[tiled_s];
+    so[canon_s + 1] = si[tiled_s + 1];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_v_layout(int to_tiled, const uint8_t* codes_in, const uint8_t* scales_in, uint8_t* codes_out,
+                           uint8_t* scales_out, int64_t B, int64_t H, int64_t N, int64_t d, hipStream_t stream) {
+  const int64_t ntile = pad_tokens(N) / 64, total = B * H * ntile * d;
+  if (total == 0) return hipSuccess;
+  v_layout_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
+      to_tiled, codes_in, scales_in, codes_out, scales_out, B * H, ntile, (int)d);
+  return hipGetLastError();
+}
+
 }  // namespace hifa4

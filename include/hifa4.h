@@ -158,6 +158,30 @@ hifa4_status hifa4_quantize_qkv(const void* q_f16, const void* k_f16, const void
                                 uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
                                 int scale_rule, void* stream);
 
+/*
+ * V_hat layout conversion: a pure re-arrangement of the 4-bit codes and E8M0
+ * scale bytes of V_hat (the 4-bit operand of the PV GEMM, HiFA4 Abstract),
+ * no value changes, for callers that hold or want V_hat in the canonical
+ * token-blocked layout instead of the tiled one the attention kernels read.
+ *   canonical: codes [B][H][d][Npad/2], token j of channel c in byte j/2
+ *              (even token in the low nibble); scales [B][H][d][Npad/32],
+ *              one per 32 consecutive tokens;
+ *   tiled:     codes [B][H][Npad/64][d][32], scales [B][H][Npad/64][d][2]
+ *              (what hifa4_quantize_qkv writes and hifa4_attn_fwd reads): per
+ *              64-token tile and channel its two 32-token blocks, and in each
+ *              block's 16 bytes nibble k (k4..k0 in binary) holds the block's
+ *              token (k3 k2 k4 k1 k0).
+ * Npad = N rounded up to HIFA4_TOKEN_PAD.  to_tiled = 1 converts canonical
+ * -> tiled, 0 tiled -> canonical.  Each buffer holds hifa4_mx4_bytes(...)
+ * bytes; all four are device pointers, 16-byte aligned, owned by the caller;
+ * the outputs must not overlap the inputs.  EINVAL for a NULL or misaligned
+ * buffer, negative sizes or d not in {64, 128, 256}; an empty tensor is a
+ * no-op.  Asynchronous on `stream`.
+ */
+hifa4_status hifa4_v_layout(int to_tiled, const uint8_t* codes_in, const uint8_t* scales_in,
+                            uint8_t* codes_out, uint8_t* scales_out, int64_t B, int64_t H,
+                            int64_t N, int64_t d, void* stream);
+
 /* Buffers of one attention call (all device pointers). */
 typedef struct {
   /* Q: either 4-bit (row layout, from hifa4_quantize_qkv) ... */

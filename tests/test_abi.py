@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(hf):
 
 def test_status_strings_and_version(hf):
     lib = hf.load()
-    assert lib.hifa4_version() == 104
+    assert lib.hifa4_version() == 105
     for s in range(6):
         assert lib.hifa4_status_str(s)
     assert b"unknown" in lib.hifa4_status_str(99)
@@ -149,6 +149,26 @@ def test_quantize_calibrate_validation(hf, call):
         else:
             hf.hifa4_calibrate_smooth(p, None, 1, 8, 2, 16, 128, 0.5, p, p, None)
     assert e.value.status == hf.EINVAL
+
+
+@pytest.mark.parametrize("case", ["null", "bad_d", "negative", "misaligned", "overlap"])
+def test_v_layout_validation(hf, case):
+    """Argument checks of hifa4_v_layout, taken before any device access."""
+    p, q = 0x10000, 0x900000
+    args = {"null": (1, None, p, q, q + 0x40000, 1, 1, 64, 128),
+            "bad_d": (1, p, p + 0x40000, q, q + 0x40000, 1, 1, 64, 96),
+            "negative": (0, p, p + 0x40000, q, q + 0x40000, 1, -1, 64, 128),
+            "misaligned": (1, p + 8, p + 0x40000, q, q + 0x40000, 1, 1, 64, 128),
+            # the output codes start inside the input codes (1 x 1 x 128 tokens x 64 B)
+            "overlap": (1, p, p + 0x40000, p + 4096, q, 1, 1, 128, 128)}[case]
+    with pytest.raises(hf.HiFA4Error) as e:
+        hf.hifa4_v_layout(*args, None)
+    assert e.value.status == hf.EINVAL
+
+
+def test_v_layout_empty_is_noop(hf):
+    p = 0x10000
+    hf.hifa4_v_layout(1, p, p + 0x40000, 0x900000, 0x940000, 2, 3, 0, 128, None)
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

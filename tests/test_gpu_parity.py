@@ -115,6 +115,33 @@ def test_quantize_edge_values(hf):
     assert np.array_equal(to_host(v4.scales), rv[1])
 
 
+@pytest.mark.parametrize("B,H,N,d", [(2, 3, 200, 128), (1, 2, 64, 64), (1, 1, 300, 256)])
+def test_v_layout_conversion(hf, B, H, N, d):
+    """hifa4_v_layout against the oracle's canonical V_hat: canonical -> tiled equals the
+    test-side re-arrangement (tile_v) byte for byte, tiled -> canonical gives the oracle's
+    bytes back, and the quantize pass's own tiled V_hat converts to the oracle's canonical
+    V_hat (codes with +-0 equal, scales identical)."""
+    print(f"[v_layout] B={B} H={H} N={N} d={d}", flush=True)
+    rng = np.random.default_rng(N + d)
+    v = (rng.standard_normal((B, H, N, d)) * 2).astype(np.float16)
+    canon = oracle.quantize_v(v)
+    c4 = hf.MX4(to_dev(canon[0]), to_dev(canon[1]))
+    t4 = hf.v_layout(c4, to_tiled=True)
+    _sync()
+    ref_t = tile_v(canon)
+    assert np.array_equal(to_host(t4.codes), ref_t[0])
+    assert np.array_equal(to_host(t4.scales), ref_t[1])
+    back = hf.v_layout(t4, to_tiled=False)
+    _sync()
+    assert np.array_equal(to_host(back.codes), canon[0])
+    assert np.array_equal(to_host(back.scales), canon[1])
+    _, _, v4 = hf.quantize_qkv(None, None, to_dev(v), Hkv=H)
+    cq = hf.v_layout(v4, to_tiled=False)
+    _sync()
+    assert np.all(codes_equal(to_host(cq.codes), canon[0]))
+    assert np.array_equal(to_host(cq.scales), canon[1])
+
+
 # ---------------------------------------------------------------------------
 # attention forward
 # ---------------------------------------------------------------------------
