@@ -433,7 +433,9 @@ hipError_t launch_v_layout(int to_tiled, const uint8_t* codes_in, const uint8_t*
                            uint8_t* scales_out, int64_t B, int64_t H, int64_t N, int64_t d, hipStream_t stream) {
   const int64_t ntile = pad_tokens(N) / 64, total = B * H * ntile * d;
   if (total == 0) return hipSuccess;
-  v_layout_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;  // beyond one grid dimension
+  v_layout_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
       to_tiled, codes_in, scales_in, codes_out, scales_out, B * H, ntile, (int)d);
   return hipGetLastError();
 }
